@@ -1,0 +1,306 @@
+"""Pins that tie the CPU oracle to facts other than its own code.
+
+Each ``pin_*`` function takes an oracle handle (``oracle.Oracle``) and raises
+AssertionError when the oracle disagrees with the page, a closed form, an
+invariant of exact softmax attention, or an independent library evaluation.
+``test_oracle.py`` runs them on the real oracle; ``test_oracle_mutants.py``
+runs them on deliberately broken copies of the oracle source and requires every
+mutant to fail at least one of them.
+"""
+from __future__ import annotations
+
+import math
+import os
+from decimal import Decimal, getcontext
+
+import numpy as np
+import torch
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+TIGHT = 1e-12
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _close(a, b, tol, what):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} != {b.shape}"
+    assert np.all(np.isfinite(a)), f"{what}: non-finite values"
+    err = np.max(np.abs(a - b) / np.maximum(1.0, np.abs(b))) if a.size else 0.0
+    assert err <= tol, f"{what}: max scaled error {err:.3e} > {tol:.1e}"
+
+
+def load_worked_example():
+    """Parse the worked-example fixture: dict of name -> list of floats."""
+    out = {}
+    with open(os.path.join(GOLDEN, "t5_worked_example.txt"), encoding="utf-8") as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            key, *vals = line.split()
+            out[key] = [float(x) for x in vals]
+    return out
+
+
+def online_blocked(scores, values, block_n):
+    """The page's streaming update for one query row, in plain Python floats.
+
+    Running max m, running denominator l and running numerator u; each block of
+    ``block_n`` keys rescales the old state by alpha = exp(m_old - m_new)
+    ("从零训练语言模型（第二部分）", section "安全 / 在线 softmax").  Returns
+    (o, lse, alphas) with one alpha per block.
+    """
+    m, l, u = -math.inf, 0.0, 0.0
+    alphas = []
+    for start in range(0, len(scores), block_n):
+        blk = scores[start:start + block_n]
+        vb = values[start:start + block_n]
+        m_new = max(m, max(blk))
+        alpha = math.exp(m - m_new)
+        p = [math.exp(s - m_new) for s in blk]
+        l = alpha * l + sum(p)
+        u = alpha * u + sum(pi * vi for pi, vi in zip(p, vb))
+        m = m_new
+        alphas.append(alpha)
+    return u / l, m + math.log(l), alphas
+
+
+def _decimal_softmax_average(scores, values, digits=40):
+    """sum_j e^{s_j} v_j / sum_j e^{s_j} and ln sum_j e^{s_j}, in `digits`-digit decimal arithmetic."""
+    getcontext().prec = digits
+    w = [Decimal(s).exp() for s in scores]
+    den = sum(w)
+    num = sum(wi * Decimal(vi) for wi, vi in zip(w, values))
+    return float(num / den), float(den.ln())
+
+
+# ---------------------------------------------------------------- the pins
+
+
+def pin_worked_example(orc):
+    """"T5 讲解", section ④: scores [1,2,3,0], v [10,20,30,40], BLOCK_N=2, round-1 alpha = 0."""
+    ex = load_worked_example()
+    scores, values = ex["scores"], ex["values"]
+    block_n = int(ex["block_n"][0])
+    # realise the scores with D = 1, q = 1, k_j = s_j, scale = 1
+    q = np.ones((1, 1, 1, 1))
+    k = np.array(scores).reshape(1, 1, 4, 1)
+    v = np.array(values).reshape(1, 1, 4, 1)
+    # one query against four keys: pad Q to four identical rows so the shapes agree
+    q4 = np.repeat(q, 4, axis=2)
+    o, lse = orc.attention(q4, k, v, False, 1.0)
+    o_blk, lse_blk, alphas = online_blocked(scores, values, block_n)
+    assert alphas[0] == ex["alpha_round1"][0], f"round-1 alpha {alphas[0]} != page's 0"
+    o_dec, lse_dec = _decimal_softmax_average(scores, values)
+    for row in range(4):
+        _close(o[0, 0, row, 0], o_dec, TIGHT, "worked example O vs decimal")
+        _close(o[0, 0, row, 0], o_blk, TIGHT, "worked example O vs blocked recurrence")
+        _close(lse[0, 0, row], lse_dec, TIGHT, "worked example lse vs decimal")
+        _close(lse[0, 0, row], lse_blk, TIGHT, "worked example lse vs blocked recurrence")
+    # the natural-log lse, not the base-2 lse some kernels store internally
+    base2 = max(scores) / math.log(2) + math.log2(sum(math.exp(s - max(scores)) for s in scores))
+    assert abs(lse[0, 0, 0] - base2) > 1.0
+
+
+def _rand(shape, seed, scale=1.0):
+    return _rng(seed).standard_normal(shape) * scale
+
+
+def _scores(q, k, scale):
+    # independent evaluation of the score matrix (numpy matmul)
+    return scale * np.matmul(q, np.swapaxes(k, -1, -2))
+
+
+def _mask(S, causal):
+    if not causal:
+        return np.ones((S, S), dtype=bool)
+    return np.tril(np.ones((S, S), dtype=bool))
+
+
+def pin_normalisation(orc):
+    """sum_{j in J} exp(s_j - lse_i) = 1 for every row (pins p and lse together)."""
+    for causal in (False, True):
+        B, H, S, D = 2, 3, 37, 8
+        q, k, v = (_rand((B, H, S, D), 10 + t) for t in range(3))
+        scale = 0.3
+        _, lse = orc.attention(q, k, v, causal, scale)
+        s = _scores(q, k, scale)
+        w = np.exp(s - lse[..., None]) * _mask(S, causal)
+        _close(w.sum(-1), np.ones((B, H, S)), 1e-12, f"row sums (causal={causal})")
+
+
+def pin_convex_hull(orc):
+    """Each o[i,d] lies between the min and max of v[j,d] over attended j."""
+    for causal in (False, True):
+        B, H, S, D = 1, 2, 29, 5
+        q, k, v = (_rand((B, H, S, D), 20 + t, 2.0) for t in range(3))
+        o, _ = orc.attention(q, k, v, causal, 0.7)
+        for i in range(S):
+            vis = v[:, :, : i + 1, :] if causal else v
+            lo, hi = vis.min(axis=2), vis.max(axis=2)
+            assert np.all(o[:, :, i, :] >= lo - 1e-12) and np.all(o[:, :, i, :] <= hi + 1e-12), \
+                f"row {i} outside the convex hull (causal={causal})"
+
+
+def pin_permutation(orc):
+    """Non-causal O and lse are unchanged by a joint permutation of the K and V rows."""
+    B, H, S, D = 2, 2, 23, 6
+    q, k, v = (_rand((B, H, S, D), 30 + t) for t in range(3))
+    perm = _rng(39).permutation(S)
+    o1, l1 = orc.attention(q, k, v, False, 0.5)
+    o2, l2 = orc.attention(q, k[:, :, perm], v[:, :, perm], False, 0.5)
+    _close(o1, o2, 1e-12, "O under K/V permutation")
+    _close(l1, l2, 1e-12, "lse under K/V permutation")
+
+
+def pin_key_shift(orc):
+    """Adding u to every key row leaves O unchanged and shifts lse_i by scale * <q_i, u>."""
+    for causal in (False, True):
+        B, H, S, D = 1, 2, 19, 4
+        q, k, v = (_rand((B, H, S, D), 40 + t) for t in range(3))
+        u = _rand((D,), 44, 1.5)
+        scale = 0.6
+        o1, l1 = orc.attention(q, k, v, causal, scale)
+        o2, l2 = orc.attention(q, k + u, v, causal, scale)
+        _close(o2, o1, 1e-11, "O under key shift")
+        _close(l2, l1 + scale * (q @ u), 1e-11, "lse under key shift")
+
+
+def pin_uniform_scores(orc):
+    """Q = 0 makes every score 0: O is the mean of the attended V rows, lse = ln|J|."""
+    B, H, S, D = 2, 1, 17, 3
+    v = _rand((B, H, S, D), 50)
+    k = _rand((B, H, S, D), 51)
+    q = np.zeros((B, H, S, D))
+    o, lse = orc.attention(q, k, v, False, 0.9)
+    _close(o, np.broadcast_to(v.mean(axis=2, keepdims=True), o.shape), 1e-12, "uniform O")
+    _close(lse, np.full((B, H, S), math.log(S)), 1e-12, "uniform lse")
+    o, lse = orc.attention(q, k, v, True, 0.9)
+    prefix = np.cumsum(v, axis=2) / np.arange(1, S + 1)[None, None, :, None]
+    _close(o, prefix, 1e-12, "causal uniform O (prefix mean)")
+    _close(lse, np.broadcast_to(np.log(np.arange(1, S + 1)), (B, H, S)), 1e-12, "causal uniform lse")
+
+
+def pin_causal_row0(orc):
+    """Causal row 0 sees only key 0: O[0] = V[0] and lse[0] = scale * <q_0, k_0>."""
+    B, H, S, D = 2, 2, 11, 7
+    q, k, v = (_rand((B, H, S, D), 60 + t) for t in range(3))
+    o, lse = orc.attention(q, k, v, True, 0.45)
+    _close(o[:, :, 0], v[:, :, 0], 1e-12, "causal row 0 O")
+    _close(lse[:, :, 0], 0.45 * np.sum(q[:, :, 0] * k[:, :, 0], axis=-1), 1e-12, "causal row 0 lse")
+
+
+def pin_single_key(orc):
+    """S = 1: O = V and lse = scale * <q, k>, causal or not."""
+    for causal in (False, True):
+        q, k, v = (_rand((3, 2, 1, 5), 70 + t) for t in range(3))
+        o, lse = orc.attention(q, k, v, causal, 1.3)
+        _close(o, v, 1e-12, "S=1 O")
+        _close(lse, 1.3 * np.sum(q * k, axis=-1), 1e-12, "S=1 lse")
+
+
+def pin_last_row_agrees(orc):
+    """Row S-1 attends to every key with or without the causal mask."""
+    B, H, S, D = 2, 2, 33, 6
+    q, k, v = (_rand((B, H, S, D), 80 + t) for t in range(3))
+    o1, l1 = orc.attention(q, k, v, False, 0.4)
+    o2, l2 = orc.attention(q, k, v, True, 0.4)
+    _close(o2[:, :, -1], o1[:, :, -1], 1e-13, "last row O, causal vs not")
+    _close(l2[:, :, -1], l1[:, :, -1], 1e-13, "last row lse, causal vs not")
+
+
+def pin_torch_reference(orc):
+    """Tiny shapes against torch's float64 softmax and logsumexp on an explicitly masked score matrix."""
+    seed = 90
+    for causal in (False, True):
+        for (B, H, S, D) in [(1, 1, 1, 1), (1, 2, 3, 2), (2, 1, 5, 3), (1, 3, 8, 4), (2, 2, 7, 4)]:
+            q, k, v = (_rand((B, H, S, D), seed + t) for t in range(3))
+            seed += 3
+            scale = 1.0 / math.sqrt(D)
+            o, lse = orc.attention(q, k, v, causal, scale)
+            tq, tk, tv = (torch.from_numpy(x) for x in (q, k, v))
+            s = torch.matmul(tq, tk.transpose(-1, -2)) * scale
+            if causal:
+                s = s.masked_fill(~torch.from_numpy(_mask(S, True)), float("-inf"))
+            ref_o = torch.matmul(torch.softmax(s, dim=-1), tv).numpy()
+            ref_l = torch.logsumexp(s, dim=-1).numpy()
+            _close(o, ref_o, 1e-12, f"O vs torch {B,H,S,D} causal={causal}")
+            _close(lse, ref_l, 1e-12, f"lse vs torch {B,H,S,D} causal={causal}")
+
+
+def pin_large_scores(orc):
+    """Scores of magnitude ~1e3 must not overflow: compare with torch's stable float64 softmax."""
+    for causal in (False, True):
+        B, H, S, D = 1, 2, 12, 4
+        q, k, v = (_rand((B, H, S, D), 120 + t) for t in range(3))
+        scale = 400.0
+        o, lse = orc.attention(q, k, v, causal, scale)
+        tq, tk, tv = (torch.from_numpy(x) for x in (q, k, v))
+        s = torch.matmul(tq, tk.transpose(-1, -2)) * scale
+        if causal:
+            s = s.masked_fill(~torch.from_numpy(_mask(S, True)), float("-inf"))
+        _close(o, torch.matmul(torch.softmax(s, dim=-1), tv).numpy(), 1e-12, "large-score O")
+        _close(lse, torch.logsumexp(s, dim=-1).numpy(), 1e-12, "large-score lse")
+
+
+def pin_heads_independent(orc):
+    """Each (b, h) slice of a [B,H,S,D] call equals a call on that slice alone."""
+    for causal in (False, True):
+        B, H, S, D = 2, 3, 9, 4
+        q, k, v = (_rand((B, H, S, D), 130 + t) for t in range(3))
+        o, lse = orc.attention(q, k, v, causal, 0.5)
+        for b in range(B):
+            for h in range(H):
+                sl = (slice(b, b + 1), slice(h, h + 1))
+                o1, l1 = orc.attention(q[sl], k[sl], v[sl], causal, 0.5)
+                _close(o[sl], o1, 0.0, f"head ({b},{h}) O")
+                _close(lse[sl], l1, 0.0, f"head ({b},{h}) lse")
+
+
+def pin_rows_entry(orc):
+    """The row-sampling entry point returns exactly the rows of the full call, in the order asked."""
+    for causal in (False, True):
+        B, H, S, D = 2, 2, 21, 5
+        q, k, v = (_rand((B, H, S, D), 140 + t) for t in range(3))
+        o, lse = orc.attention(q, k, v, causal, 0.8)
+        rows = np.array([0, 5, B * H * S - 1, 22, 41, 20, 63], dtype=np.int64)
+        orow, lrow = orc.attention_rows(q, k, v, causal, 0.8, rows)
+        _close(orow, o.reshape(-1, D)[rows], 0.0, "rows entry O")
+        _close(lrow, lse.reshape(-1)[rows], 0.0, "rows entry lse")
+
+
+def pin_one_hot(orc):
+    """A key aligned with the query and scaled up dominates: O -> that key's value row."""
+    S, D = 6, 4
+    k = _rand((1, 1, S, D), 150, 0.1)
+    k[0, 0, 3] = np.eye(D)[0]
+    v = _rand((1, 1, S, D), 151)
+    q = np.zeros((1, 1, S, D))
+    q[0, 0, :, :] = k[0, 0, 3, :] * 50.0  # every query points at key 3
+    o, _ = orc.attention(q, k, v, False, 1.0)
+    gap = 50.0 * (np.sum(k[0, 0, 3] ** 2) - np.max(np.delete(k[0, 0] @ k[0, 0, 3], 3)))
+    assert gap > 40.0
+    _close(o[0, 0], np.broadcast_to(v[0, 0, 3], (S, D)), 1e-12, "one-hot O")
+
+
+ALL_PINS = [
+    pin_worked_example,
+    pin_normalisation,
+    pin_convex_hull,
+    pin_permutation,
+    pin_key_shift,
+    pin_uniform_scores,
+    pin_causal_row0,
+    pin_single_key,
+    pin_last_row_agrees,
+    pin_torch_reference,
+    pin_large_scores,
+    pin_heads_independent,
+    pin_rows_entry,
+    pin_one_hot,
+]

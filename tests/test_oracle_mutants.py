@@ -1,0 +1,65 @@
+"""Every plausible slip in the oracle must fail at least one pin.
+
+Each case copies ``oracle/attn_oracle.c``, plants one mistake by text
+replacement (a dropped term, a wrong sign, a wrong index, a transposed operand,
+an off-by-one mask, a wrong log base), compiles the copy into a temporary
+directory and runs the pin suite on it.  The real oracle is never modified.
+"""
+import os
+
+import pytest
+
+import oracle
+import oracle_pins
+
+MUTANTS = {
+    "dot_wrong_index": ("dot += q_i[d] * k_j[d];", "dot += q_i[d] * k_j[0];"),
+    "dropped_scale": ("p[j] = scale * dot;", "p[j] = dot;"),
+    "min_not_max": ("if (p[j] > m)", "if (p[j] < m)"),
+    "no_max_subtraction": ("p[j] = exp(p[j] - m);", "p[j] = exp(p[j]);"),
+    "exp_sign_flip": ("p[j] = exp(p[j] - m);", "p[j] = exp(m - p[j]);"),
+    "pv_wrong_index": ("acc[d] += p[j] * v_j[d];", "acc[d] += p[j] * v_j[0];"),
+    "no_normalisation": ("o_i[d] = acc[d] / l;", "o_i[d] = acc[d];"),
+    "lse_base2": ("*lse_i = m + log(l);", "*lse_i = m + log2(l);"),
+    "lse_drops_max": ("*lse_i = m + log(l);", "*lse_i = log(l);"),
+    "causal_off_by_one": ("causal ? i + 1 : S", "causal ? (i > 0 ? i : 1) : S"),
+    "causal_wrong_triangle": ("causal ? i + 1 : S", "causal ? S - i : S"),
+    "k_transposed": ("const double *k_j = k_bh + j * D;", "const double *k_j = k_bh + j;"),
+    "v_transposed": ("const double *v_j = v_bh + j * D;", "const double *v_j = v_bh + j;"),
+    "k_head_offset_dropped": ("k + bh * S * D", "k"),
+    "v_head_offset_dropped": ("v + bh * S * D", "v"),
+    "acc_init_one": ("acc[d] = 0.0;", "acc[d] = 1.0;"),
+    "l_init_one": ("double l = 0.0;", "double l = 1.0;"),
+    "q_row_offset": ("q + flat * D", "q + bh * S * D"),
+}
+
+
+@pytest.fixture(scope="module")
+def source():
+    with open(oracle.SOURCE, encoding="utf-8") as f:
+        return f.read()
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, source, tmp_path):
+    old, new = MUTANTS[name]
+    assert old in source, f"mutation site for {name!r} no longer exists in the oracle source"
+    src = tmp_path / f"{name}.c"
+    src.write_text(source.replace(old, new), encoding="utf-8")
+    lib = oracle.build(str(src), str(tmp_path / f"lib{name}.so"))
+    mutant = oracle.Oracle(lib)
+    failures = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(mutant)
+        except (AssertionError, ValueError, FloatingPointError) as e:
+            failures.append(pin.__name__)
+    assert failures, f"mutant {name!r} passed every pin"
+
+
+def test_unmutated_copy_passes(source, tmp_path):
+    src = tmp_path / "same.c"
+    src.write_text(source, encoding="utf-8")
+    same = oracle.Oracle(oracle.build(str(src), str(tmp_path / "libsame.so")))
+    for pin in oracle_pins.ALL_PINS:
+        pin(same)
