@@ -1,0 +1,171 @@
+#!/usr/bin/env python3
+"""Benchmark of the FlashAttention-2 forward on one MI355X.
+
+One step = one forward pass (one fa_fwd launch) over the multi-head causal
+workload B=4, H=16, S=4096, D=64, fp16, [B,H,S,D] layout, with q, k, v drawn
+from a fixed seed and resident in HBM before timing starts.  The metric is
+attention-forward TFLOP/s with FLOPs = 4*B*H*S^2*D, halved for causal, and its
+fraction of the MI355X dense fp16 matrix peak (2.5 PFLOP/s).
+
+Prints one JSON line.  Also reported:
+  roofline      achieved TFLOP/s of the attention kernel from HIP events around
+                every timed launch on the stream it runs on, against the peak;
+                `traffic` is filled from rocprofv3 counters when given
+                (--traffic-bytes) and null otherwise;
+  cpu_baseline  the float64 CPU oracle timed on this host's cores over the
+                whole workload (every row of every head), in the same unit.
+
+Options: --gpus N (only 1 is supported: the kernel runs on one GPU),
+--steps K (timed launches), --warmup W, --workload NAME, --no-cpu-baseline,
+--sweep FILE (also time every named workload and write one JSON line per
+workload to FILE).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_MFMA_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "f32": 157.3}  # dense, MI355X published
+PEAK_HBM_GBS = 8000.0
+
+
+def time_workload(fa, torch, w, causal, steps, warmup):
+    import workloads
+    q, k, v = (x.to("cuda:0") for x in workloads.workload_inputs(w))
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.S), dtype=torch.float32, device="cuda:0")
+    for _ in range(warmup):
+        fa.forward(q, k, v, causal=causal, scale=w.scale, out=o, lse=lse)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        fa.forward(q, k, v, causal=causal, scale=w.scale, out=o, lse=lse)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    return wall, kernel_ms
+
+
+def cpu_baseline(w, causal):
+    import numpy as np
+    import oracle
+    import workloads
+    orc = oracle.default()
+    q, k, v = workloads.workload_inputs(w)
+    q, k, v = (x.double().numpy() for x in (q, k, v))
+    t0 = time.perf_counter()
+    orc.attention(q, k, v, causal, w.scale)
+    dt = time.perf_counter() - t0
+    return {
+        "value": w.flops(causal) / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": orc.num_threads(),
+        "kind": "oracle",
+        "sample": f"whole workload ({w.B * w.H * w.S} rows, float64, {dt:.2f} s wall)",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="multihead_causal")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic-bytes", type=float, default=None,
+                    help="HBM bytes per launch measured with rocprofv3 counters")
+    ap.add_argument("--sweep", default=None, help="write per-workload JSON lines to this file")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: --gpus {args.gpus} is not supported; this attention forward runs on one GPU "
+              "(no sharding or collectives are built). Use --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+    import exact_tiled_attention_06_amd as fa
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+
+    w = workloads.BY_NAME[args.workload]
+    causal = w.causal[-1]
+    wall, kernel_ms = time_workload(fa, torch, w, causal, args.steps, args.warmup)
+    flops = w.flops(causal)
+    ms_per_step = wall * 1e3 / args.steps
+    value = flops / (wall / args.steps) / 1e12
+    avg_kernel_ms = sum(kernel_ms) / len(kernel_ms)
+    achieved = flops / (avg_kernel_ms * 1e-3) / 1e12
+    peak = PEAK_MFMA_TFLOPS[w.dtype]
+    out = {
+        "metric": "attention fwd TFLOP/s and % of MI355X dense fp16/bf16 MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "pct_of_peak": round(100.0 * value / peak, 2),
+        "config": {
+            "workload": f"{w.name}: B={w.B} H={w.H} S={w.S} D={w.D} {w.dtype} "
+                        f"{'causal' if causal else 'non-causal'}, [B,H,S,D], randn seed {w.seed}",
+            "B": w.B, "H": w.H, "S": w.S, "D": w.D, "causal": causal,
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4),
+            "traffic": args.traffic_bytes,
+            "kernel_ms_avg": round(avg_kernel_ms, 5),
+            "kernel_ms_min": round(min(kernel_ms), 5),
+            "hbm_gbs_algorithmic": round(w.hbm_bytes() / (avg_kernel_ms * 1e-3) / 1e9, 1),
+        },
+        "cpu_baseline": None,
+    }
+
+    if args.sweep:
+        with open(args.sweep, "w") as f:
+            for sw in workloads.ALL:
+                for c in sw.causal:
+                    wl, kms = time_workload(fa, torch, sw, c, max(10, args.steps // 4), 5)
+                    avg = sum(kms) / len(kms)
+                    rec = {"workload": sw.name, "causal": c, "dtype": sw.dtype, "B": sw.B, "H": sw.H,
+                           "S": sw.S, "D": sw.D, "kernel_ms_avg": avg,
+                           "tflops": sw.flops(c) / (avg * 1e-3) / 1e12,
+                           "pct_peak": 100 * sw.flops(c) / (avg * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS[sw.dtype],
+                           "hbm_gbs": sw.hbm_bytes() / (avg * 1e-3) / 1e9}
+                    f.write(json.dumps(rec) + "\n")
+                    print(f"sweep {sw.name} causal={c}: {rec['tflops']:.1f} TFLOP/s "
+                          f"({avg * 1e3:.1f} us)", file=sys.stderr, flush=True)
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, causal)
+
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,128 @@
+"""FlashAttention-2 forward for AMD Instinct MI355X (gfx950): Python binding of libfa.so.
+
+Argument marshalling only: every step of the attention runs in the HIP kernels
+behind the C ABI declared in ``include/fa.h``.  PyTorch supplies device memory
+and the current stream; this module never computes attention itself and has no
+CPU fallback -- importing it fails loudly when the library is not built.
+
+    fa_fwd(q, k, v, o, lse, B, H, S, D, causal, scale, dtype, stream)
+        the C entry point with raw device pointers (ints) and sizes;
+    fa_status_string(status)
+        the C status description;
+    forward(q, k, v, causal=False, scale=None) -> (o, lse)
+        convenience on torch tensors [B,H,S,D]: allocates o (input dtype) and
+        lse (float32 [B,H,S]) and calls fa_fwd on the current stream.  The
+        default scale is 1/sqrt(D) ("T5 讲解：FlashAttention forward", section ⑥).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch  # loads the HIP runtime that libfa.so binds to (same soname)
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(_HERE, "libfa.so")
+
+FA_OK = 0
+FA_ERR_NULL_POINTER = 1
+FA_ERR_SHAPE = 2
+FA_ERR_HEAD_DIM = 3
+FA_ERR_DTYPE = 4
+FA_ERR_CAUSAL = 5
+FA_ERR_SCALE = 6
+FA_ERR_ALIAS = 7
+FA_ERR_TOO_LARGE = 8
+FA_ERR_LAUNCH = 9
+FA_ERR_ALIGNMENT = 10
+
+FA_DTYPE_F32 = 0
+FA_DTYPE_F16 = 1
+FA_DTYPE_BF16 = 2
+
+DTYPE_CODES = {torch.float32: FA_DTYPE_F32, torch.float16: FA_DTYPE_F16, torch.bfloat16: FA_DTYPE_BF16}
+
+# argument problems map to ValueError, runtime problems to RuntimeError
+_VALUE_ERRORS = {FA_ERR_NULL_POINTER, FA_ERR_SHAPE, FA_ERR_HEAD_DIM, FA_ERR_DTYPE, FA_ERR_CAUSAL,
+                 FA_ERR_SCALE, FA_ERR_ALIAS, FA_ERR_TOO_LARGE, FA_ERR_ALIGNMENT}
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIBRARY):
+        raise ImportError(
+            f"{LIBRARY} is not built; build it with `python -m exact_tiled_attention_06_amd.build` "
+            "(there is no CPU fallback)")
+    lib = ctypes.CDLL(LIBRARY)
+    lib.fa_fwd.restype = ctypes.c_int
+    lib.fa_fwd.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_void_p] + [ctypes.c_int64] * 4 + [
+        ctypes.c_int, ctypes.c_float, ctypes.c_int, ctypes.c_void_p]
+    lib.fa_status_string.restype = ctypes.c_char_p
+    lib.fa_status_string.argtypes = [ctypes.c_int]
+    return lib
+
+
+_lib = _load()
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int):
+        super().__init__(f"fa_fwd failed: {fa_status_string(status)} (status {status})")
+        self.status = status
+
+
+class FaValueError(ValueError):
+    def __init__(self, status: int):
+        super().__init__(f"fa_fwd rejected its arguments: {fa_status_string(status)} (status {status})")
+        self.status = status
+
+
+def fa_status_string(status: int) -> str:
+    return _lib.fa_status_string(int(status)).decode()
+
+
+def fa_fwd(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, S: int, D: int,
+           causal: int, scale: float, dtype: int, stream: int) -> int:
+    """The C entry point: raw device addresses and sizes; returns the status code."""
+    return int(_lib.fa_fwd(q, k, v, o, lse, B, H, S, D, int(causal), float(scale), int(dtype), stream))
+
+
+def check(status: int) -> None:
+    if status == FA_OK:
+        return
+    if status in _VALUE_ERRORS:
+        raise FaValueError(status)
+    raise FaError(status)
+
+
+def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+            scale: float | None = None, out: torch.Tensor | None = None,
+            lse: torch.Tensor | None = None):
+    """Attention forward on [B,H,S,D] device tensors; returns (o, lse)."""
+    if q.dim() != 4:
+        raise ValueError(f"q must be [B,H,S,D], got shape {tuple(q.shape)}")
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError(f"q, k, v shapes differ: {tuple(q.shape)}, {tuple(k.shape)}, {tuple(v.shape)}")
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in DTYPE_CODES:
+        raise ValueError(f"q, k, v must share one of {list(DTYPE_CODES)}; got {q.dtype}, {k.dtype}, {v.dtype}")
+    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+        raise RuntimeError("q, k, v must be device tensors")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k, v must be contiguous")
+    B, H, S, D = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    scale = float(torch.tensor(scale, dtype=torch.float32))
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor of q's shape and dtype")
+    if lse.shape != (B, H, S) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 tensor of shape [B,H,S]")
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    status = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                    B, H, S, D, int(bool(causal)), scale, DTYPE_CODES[q.dtype], stream)
+    check(status)
+    return out, lse

@@ -1,0 +1,65 @@
+"""Build libfa.so (the HIP kernels and their C ABI) for gfx950 with hipcc.
+
+Usage: ``python -m exact_tiled_attention_06_amd.build`` (or ``build()`` from
+Python).  The library is written next to this file, so it travels with the
+source tree.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+SOURCES = [os.path.join(HERE, "csrc", "fa_fwd.hip")]
+HEADERS = [os.path.join(HERE, "csrc", f) for f in ("fa_common.hpp", "fa_mfma.hpp", "fa_f32.hpp")] + [
+    os.path.join(ROOT, "include", "fa.h")]
+LIBRARY = os.path.join(HERE, "libfa.so")
+
+ARCH = "gfx950"
+FLAGS = [
+    f"--offload-arch={ARCH}",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-shared",
+    # packed fp32 VALU forms stay off: plain fp32 arithmetic only
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall",
+    "-Wno-unused-command-line-argument",
+]
+
+
+def hipcc() -> str:
+    for cand in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm toolchain required to build the HIP library)")
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source into LIBRARY; always recompiles."""
+    tmp = LIBRARY + ".tmp"
+    cmd = [hipcc(), *FLAGS, "-o", tmp, *SOURCES]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{res.stderr[-8000:]}")
+    os.replace(tmp, LIBRARY)
+    return LIBRARY
+
+
+def is_stale() -> bool:
+    if not os.path.exists(LIBRARY):
+        return True
+    t = os.path.getmtime(LIBRARY)
+    return any(os.path.getmtime(f) > t for f in SOURCES + HEADERS)
+
+
+if __name__ == "__main__":
+    path = build(verbose=True)
+    print(path)
+    sys.exit(0)

@@ -1,0 +1,136 @@
+// fa_fwd.hip -- the C ABI of the attention forward library: argument checks,
+// kernel-instance selection and the launch on the caller's stream.
+//
+// Host-side plan ("T5 讲解：FlashAttention forward", sections ② and ⑥;
+// "Triton 实现", section "Grid 与并行策略"): one workgroup per
+// (query block, batch*head), i.e. ceil(S/BM) * B*H independent workgroups with
+// no communication between them; the default scale 1/sqrt(D) is the caller's
+// business (the Python binding supplies it).
+#include <math.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/fa.h"
+#include "fa_f32.hpp"
+#include "fa_mfma.hpp"
+
+namespace {
+
+using namespace fa;
+
+// Matrix-core kernel shape per head dimension: waves per workgroup, 32-query
+// blocks per wave and keys per LDS tile.
+template <int D>
+struct Tile {
+    static constexpr int NW = 4;
+    static constexpr int QB = 1;
+    static constexpr int BN = 64;
+};
+
+int64_t elem_size(int dtype) { return dtype == FA_DTYPE_F32 ? 4 : 2; }
+
+bool overlaps(const void* a, int64_t na, const void* b, int64_t nb) {
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + (uintptr_t)nb && b0 < a0 + (uintptr_t)na;
+}
+
+template <typename T, int D, bool CAUSAL>
+int launch_mfma(const void* q, const void* k, const void* v, void* o, float* lse, int S, int BH,
+                float c, hipStream_t stream) {
+    using Cfg = MfmaConfig<T, D, CAUSAL, Tile<D>::QB, Tile<D>::NW, Tile<D>::BN>;
+    const int n_qblk = (S + Cfg::BM - 1) / Cfg::BM;
+    const int64_t grid = (int64_t)n_qblk * BH;
+    if (grid > (int64_t)1 << 24) return FA_ERR_TOO_LARGE;
+    (void)hipGetLastError();  // clear a stale error so the check below sees this launch only
+    hipLaunchKernelGGL((fa_fwd_mfma_kernel<T, Cfg>), dim3((unsigned)grid), dim3(Cfg::NT), 0, stream,
+                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse,
+                       S, BH, n_qblk, c);
+    return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+template <int D, bool CAUSAL>
+int launch_f32(const void* q, const void* k, const void* v, void* o, float* lse, int S, int BH,
+               float c, hipStream_t stream) {
+    const int n_qblk = (S + F32_BM - 1) / F32_BM;
+    const int64_t grid = (int64_t)n_qblk * BH;
+    if (grid > (int64_t)1 << 24) return FA_ERR_TOO_LARGE;
+    (void)hipGetLastError();
+    hipLaunchKernelGGL((fa_fwd_f32_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(F32_BM), 0, stream,
+                       (const float*)q, (const float*)k, (const float*)v, (float*)o, lse, S, BH, n_qblk,
+                       c);
+    return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+template <int D, bool CAUSAL>
+int dispatch_dtype(int dtype, const void* q, const void* k, const void* v, void* o, float* lse, int S,
+                   int BH, float c, hipStream_t stream) {
+    switch (dtype) {
+        case FA_DTYPE_F16: return launch_mfma<F16, D, CAUSAL>(q, k, v, o, lse, S, BH, c, stream);
+        case FA_DTYPE_BF16: return launch_mfma<BF16, D, CAUSAL>(q, k, v, o, lse, S, BH, c, stream);
+        default: return launch_f32<D, CAUSAL>(q, k, v, o, lse, S, BH, c, stream);
+    }
+}
+
+template <bool CAUSAL>
+int dispatch_d(int64_t D, int dtype, const void* q, const void* k, const void* v, void* o, float* lse,
+               int S, int BH, float c, hipStream_t stream) {
+    switch (D) {
+        case 16: return dispatch_dtype<16, CAUSAL>(dtype, q, k, v, o, lse, S, BH, c, stream);
+        case 32: return dispatch_dtype<32, CAUSAL>(dtype, q, k, v, o, lse, S, BH, c, stream);
+        case 64: return dispatch_dtype<64, CAUSAL>(dtype, q, k, v, o, lse, S, BH, c, stream);
+        default: return dispatch_dtype<128, CAUSAL>(dtype, q, k, v, o, lse, S, BH, c, stream);
+    }
+}
+
+}  // namespace
+
+extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                      int64_t H, int64_t S, int64_t D, int causal, float scale, int dtype,
+                      void* stream) {
+    // ---- argument checks: no HIP call before all of them pass ----------------
+    if (B < 0 || H < 0 || S < 0) return FA_ERR_SHAPE;
+    if (D != 16 && D != 32 && D != 64 && D != 128) return FA_ERR_HEAD_DIM;
+    if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
+    if (causal != 0 && causal != 1) return FA_ERR_CAUSAL;
+    if (!isfinite(scale) || !(scale > 0.f)) return FA_ERR_SCALE;
+    if (B == 0 || H == 0 || S == 0) return FA_OK;  // empty problem: nothing to compute
+    if (!q || !k || !v || !o || !lse) return FA_ERR_NULL_POINTER;
+    // index ranges: heads*S must fit the kernels' int arithmetic, S*D per head int64
+    const int64_t kMaxInt = 2147483647;
+    if (B > kMaxInt || H > kMaxInt || B * H > kMaxInt / 2 || S > (kMaxInt >> 1)) return FA_ERR_TOO_LARGE;
+    const int64_t BH = B * H;
+    if (BH > INT64_MAX / S || BH * S > INT64_MAX / (D * 8)) return FA_ERR_TOO_LARGE;
+    const int64_t tensor_bytes = BH * S * D * elem_size(dtype);
+    const int64_t lse_bytes = BH * S * 4;
+    if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15) return FA_ERR_ALIGNMENT;
+    if (((uintptr_t)lse) & 3) return FA_ERR_ALIGNMENT;
+    if (overlaps(o, tensor_bytes, q, tensor_bytes) || overlaps(o, tensor_bytes, k, tensor_bytes) ||
+        overlaps(o, tensor_bytes, v, tensor_bytes) || overlaps(o, tensor_bytes, lse, lse_bytes) ||
+        overlaps(lse, lse_bytes, q, tensor_bytes) || overlaps(lse, lse_bytes, k, tensor_bytes) ||
+        overlaps(lse, lse_bytes, v, tensor_bytes))
+        return FA_ERR_ALIAS;
+
+    // c = scale * log2(e), rounded once to fp32: scores enter exp2 as S*c - m.
+    const float c = (float)((double)scale * 1.4426950408889634);
+    hipStream_t st = (hipStream_t)stream;
+    return causal ? dispatch_d<true>(D, dtype, q, k, v, o, lse, (int)S, (int)BH, c, st)
+                  : dispatch_d<false>(D, dtype, q, k, v, o, lse, (int)S, (int)BH, c, st);
+}
+
+extern "C" const char* fa_status_string(int status) {
+    switch (status) {
+        case FA_OK: return "ok";
+        case FA_ERR_NULL_POINTER: return "a tensor pointer is NULL";
+        case FA_ERR_SHAPE: return "B, H and S must be >= 0";
+        case FA_ERR_HEAD_DIM: return "head dim D must be 16, 32, 64 or 128";
+        case FA_ERR_DTYPE: return "dtype must be FA_DTYPE_F32, FA_DTYPE_F16 or FA_DTYPE_BF16";
+        case FA_ERR_CAUSAL: return "causal must be 0 or 1";
+        case FA_ERR_SCALE: return "scale must be finite and > 0";
+        case FA_ERR_ALIAS: return "o and lse must not overlap each other or q, k, v";
+        case FA_ERR_TOO_LARGE: return "problem size exceeds the kernels' index ranges";
+        case FA_ERR_LAUNCH: return "the HIP runtime rejected the kernel launch";
+        case FA_ERR_ALIGNMENT: return "q, k, v, o must be 16-byte aligned and lse 4-byte aligned";
+        default: return "unknown status";
+    }
+}

@@ -1,0 +1,101 @@
+/*
+ * fa.h -- FlashAttention-2 forward pass for AMD Instinct MI355X (gfx950).
+ *
+ * One call computes exact attention for every (batch, head):
+ *
+ *     O   = softmax(Q K^T * scale) V
+ *     lse = m + ln(l)      per query row (m: row maximum of the scaled scores,
+ *                          l: sum of exp(score - m) over the attended keys)
+ *
+ * with query blocks as the outer loop and key/value blocks streamed through an
+ * inner loop under an online softmax (running maximum, running sum and an fp32
+ * output accumulator rescaled by exp(m_old - m_new)).  The [S,S] score and
+ * probability matrices never reach device memory; only O and lse are written.
+ *
+ * Where the operation is defined on the pages:
+ *   - the attention definition and the [B,H,S,D] layout: "T5 讲解：
+ *     FlashAttention forward", section ① ;
+ *   - the Q-outer / K,V-inner loop with the running m, l, acc state and the
+ *     rescale factor alpha: same page, sections ③-④ ; "Triton 实现", sections
+ *     "Q-outer 主循环" and "内层循环" ; "从零训练语言模型（第二部分）", section
+ *     "安全 / 在线 softmax" ;
+ *   - causal masking (query i sees keys 0..i) split into off-band blocks with
+ *     no mask and on-band diagonal blocks with a mask: "Triton 实现", section
+ *     "Causal Mask 的处理：off-band 与 on-band" ; "T5 讲解", section ⑤ ;
+ *   - the saved lse = m + log l: "Inside FlashAttention", section 2.4 ;
+ *     "T5 讲解", section ⑥ ;
+ *   - the default scale 1/sqrt(D) and head dims 16..128: "T5 讲解", section ⑥.
+ *
+ * Thread safety: calls are independent; the library keeps no state besides
+ * the kernels' code objects and allocates, frees and synchronises nothing.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------- */
+#define FA_OK 0
+#define FA_ERR_NULL_POINTER 1   /* a tensor pointer is NULL for a non-empty problem */
+#define FA_ERR_SHAPE 2          /* B, H or S is negative */
+#define FA_ERR_HEAD_DIM 3       /* D is not 16, 32, 64 or 128 */
+#define FA_ERR_DTYPE 4          /* dtype is not FA_DTYPE_F32 / _F16 / _BF16 */
+#define FA_ERR_CAUSAL 5         /* causal is not 0 or 1 */
+#define FA_ERR_SCALE 6          /* scale is not finite or not > 0 */
+#define FA_ERR_ALIAS 7          /* o or lse overlaps q, k, v or each other */
+#define FA_ERR_TOO_LARGE 8      /* sizes overflow the kernels' index ranges */
+#define FA_ERR_LAUNCH 9         /* the HIP runtime rejected the kernel launch */
+#define FA_ERR_ALIGNMENT 10     /* q, k, v, o not 16-byte aligned, or lse not 4-byte aligned */
+
+/* ---- element types (the dtype argument) --------------------------------- */
+#define FA_DTYPE_F32 0
+#define FA_DTYPE_F16 1
+#define FA_DTYPE_BF16 2
+
+/*
+ * fa_fwd -- attention forward over B*H independent (batch, head) problems.
+ *
+ *   q, k, v  device pointers to contiguous [B,H,S,D] tensors of `dtype`
+ *            (row-major, last dimension contiguous, 16-byte aligned; they
+ *            may alias one another, e.g. q == k).
+ *   o        device pointer to a contiguous [B,H,S,D] output of `dtype`.
+ *   lse      device pointer to a contiguous [B,H,S] float32 output: the
+ *            natural-log log-sum-exp of each query row's scaled scores.
+ *   B, H, S  batch, heads, sequence length (queries = keys = S).  Any of them
+ *            may be 0 (an empty problem: nothing is launched, FA_OK).
+ *   D        head dimension: 16, 32, 64 or 128.
+ *   causal   0: every query sees every key; 1: query i sees keys 0..i.
+ *   scale    score multiplier, finite and > 0 (callers normally pass
+ *            1/sqrt(D) rounded to float32).
+ *   dtype    FA_DTYPE_F16 / FA_DTYPE_BF16: both contractions run on the
+ *            matrix cores with fp32 accumulation; the softmax weights are
+ *            rounded to dtype (nearest-even) before the P*V product.
+ *            FA_DTYPE_F32: all arithmetic in fp32.
+ *   stream   hipStream_t to enqueue on (NULL = the default stream).
+ *
+ * Ownership: the caller allocates all five buffers; o and lse must not
+ * overlap each other or the inputs.  The library never allocates, frees or
+ * synchronises: the kernel is enqueued on `stream` and the call returns at
+ * once, so results are ready once the stream reaches that point.
+ *
+ * Errors: argument checks run before any HIP call and return the FA_ERR_*
+ * code of the first failed check, writing nothing.  FA_ERR_LAUNCH reports a
+ * launch rejected by the runtime (hipGetLastError); faults during execution
+ * surface on the stream, as for any kernel.
+ */
+int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
+           int64_t B, int64_t H, int64_t S, int64_t D,
+           int causal, float scale, int dtype, void *stream);
+
+/* A static, human-readable description of a status code (never NULL). */
+const char *fa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

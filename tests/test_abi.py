@@ -1,0 +1,126 @@
+"""The C ABI library on the CPU: it loads, exports every declared symbol, and
+rejects bad arguments with the documented status codes before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+
+def _header_text():
+    with open(HEADER, encoding="utf-8") as f:
+        return f.read()
+
+
+def _declared_functions():
+    text = re.sub(r"/\*.*?\*/", "", _header_text(), flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_\w+)\s*\(", text)))
+
+
+def _defines():
+    return {m.group(1): int(m.group(2)) for m in re.finditer(r"#define\s+(FA_\w+)\s+(-?\d+)", _header_text())}
+
+
+@pytest.fixture(scope="module")
+def fa():
+    import exact_tiled_attention_06_amd as fa
+    return fa
+
+
+@pytest.fixture(scope="module")
+def lib(fa):
+    return ctypes.CDLL(fa.LIBRARY)
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared_functions()
+    assert "fa_fwd" in names and "fa_status_string" in names
+    for name in names:
+        assert hasattr(lib, name), f"{name} declared in include/fa.h but not exported"
+
+
+def test_binding_constants_match_header(fa):
+    for name, value in _defines().items():
+        assert getattr(fa, name) == value, name
+
+
+def test_status_strings(fa):
+    codes = [v for k, v in _defines().items() if k.startswith("FA_ERR_") or k == "FA_OK"]
+    seen = set()
+    for c in codes:
+        s = fa.fa_status_string(c)
+        assert s and s != "unknown status", c
+        seen.add(s)
+    assert len(seen) == len(codes)
+    assert fa.fa_status_string(12345) == "unknown status"
+
+
+# fake, never-dereferenced addresses: every case below fails validation first
+P = 1 << 20
+ARGS = dict(q=P, k=2 * P, v=3 * P, o=4 * P, lse=5 * P, B=1, H=1, S=64, D=64, causal=0,
+            scale=0.125, dtype=1, stream=0)
+
+
+def call(fa, **over):
+    a = dict(ARGS, **over)
+    return fa.fa_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["S"], a["D"],
+                     a["causal"], a["scale"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(B=-1), "FA_ERR_SHAPE"),
+    (dict(H=-2), "FA_ERR_SHAPE"),
+    (dict(S=-64), "FA_ERR_SHAPE"),
+    (dict(D=48), "FA_ERR_HEAD_DIM"),
+    (dict(D=256), "FA_ERR_HEAD_DIM"),
+    (dict(D=0), "FA_ERR_HEAD_DIM"),
+    (dict(dtype=3), "FA_ERR_DTYPE"),
+    (dict(dtype=-1), "FA_ERR_DTYPE"),
+    (dict(causal=2), "FA_ERR_CAUSAL"),
+    (dict(scale=0.0), "FA_ERR_SCALE"),
+    (dict(scale=-0.5), "FA_ERR_SCALE"),
+    (dict(scale=float("inf")), "FA_ERR_SCALE"),
+    (dict(scale=float("nan")), "FA_ERR_SCALE"),
+    (dict(q=0), "FA_ERR_NULL_POINTER"),
+    (dict(lse=0), "FA_ERR_NULL_POINTER"),
+    (dict(o=0), "FA_ERR_NULL_POINTER"),
+    (dict(o=P + 64), "FA_ERR_ALIAS"),             # o inside q
+    (dict(lse=4 * P + 1024), "FA_ERR_ALIAS"),     # lse inside o
+    (dict(o=2 * P), "FA_ERR_ALIAS"),              # o == k
+    (dict(q=P + 8), "FA_ERR_ALIGNMENT"),
+    (dict(o=4 * P + 2), "FA_ERR_ALIGNMENT"),
+    (dict(lse=5 * P + 2), "FA_ERR_ALIGNMENT"),
+    (dict(B=1 << 31), "FA_ERR_TOO_LARGE"),
+    (dict(S=1 << 31), "FA_ERR_TOO_LARGE"),
+    (dict(B=1 << 20, H=1 << 20), "FA_ERR_TOO_LARGE"),
+])
+def test_rejects_bad_arguments(fa, over, code):
+    assert call(fa, **over) == _defines()[code]
+
+
+def test_first_failed_check_wins(fa):
+    assert call(fa, B=-1, D=48, dtype=7) == fa.FA_ERR_SHAPE
+    assert call(fa, D=48, dtype=7) == fa.FA_ERR_HEAD_DIM
+
+
+@pytest.mark.parametrize("over", [dict(B=0), dict(H=0), dict(S=0)])
+def test_empty_problem_is_a_no_op(fa, over):
+    # nothing to compute: OK without touching the (null) pointers or the device
+    assert call(fa, q=0, k=0, v=0, o=0, lse=0, **over) == fa.FA_OK
+
+
+def test_q_k_v_may_alias(fa):
+    # read-only inputs may share storage; only the output checks reject overlaps,
+    # so this call fails later, at the null lse check
+    assert call(fa, k=P, v=P, lse=0) == fa.FA_ERR_NULL_POINTER
+
+
+def test_python_errors_map(fa):
+    with pytest.raises(ValueError):
+        fa.check(fa.FA_ERR_HEAD_DIM)
+    with pytest.raises(RuntimeError):
+        fa.check(fa.FA_ERR_LAUNCH)
+    fa.check(fa.FA_OK)
