@@ -6,8 +6,8 @@
 // (query block, batch*head), i.e. ceil(S/BM) * B*H independent workgroups with
 // no communication between them; the default scale 1/sqrt(D) is the caller's
 // business (the Python binding supplies it).
-#include <math.h>
 #include <stdint.h>
+#include <string.h>
 
 #include <hip/hip_runtime.h>
 
@@ -19,14 +19,21 @@ namespace {
 
 using namespace fa;
 
-// Matrix-core kernel shape per head dimension: waves per workgroup, 32-query
-// blocks per wave and keys per LDS tile.
+// Matrix-core kernel shapes per head dimension: {32-query blocks per wave,
+// waves per workgroup, keys per LDS tile}.  The large shape reuses every K/V
+// operand read for two query blocks; the small one (64 query rows per
+// workgroup) is used when the large shape would leave CUs idle.
 template <int D>
-struct Tile {
+struct Tiles {
+    static constexpr int QB = (D == 128) ? 1 : 2;
     static constexpr int NW = 4;
-    static constexpr int QB = 1;
-    static constexpr int BN = 64;
+    static constexpr int BN = (D == 16) ? 128 : 64;
+    static constexpr int SMALL_QB = 1;
+    static constexpr int SMALL_NW = (D == 128) ? 4 : 2;
 };
+
+// Workgroups that fill the machine twice over (256 CUs, two resident per CU).
+constexpr int64_t kFullGrid = 512;
 
 int64_t elem_size(int dtype) { return dtype == FA_DTYPE_F32 ? 4 : 2; }
 
@@ -35,10 +42,9 @@ bool overlaps(const void* a, int64_t na, const void* b, int64_t nb) {
     return a0 < b0 + (uintptr_t)nb && b0 < a0 + (uintptr_t)na;
 }
 
-template <typename T, int D, bool CAUSAL>
-int launch_mfma(const void* q, const void* k, const void* v, void* o, float* lse, int S, int BH,
-                float c, hipStream_t stream) {
-    using Cfg = MfmaConfig<T, D, CAUSAL, Tile<D>::QB, Tile<D>::NW, Tile<D>::BN>;
+template <typename T, typename Cfg>
+int launch_cfg(const void* q, const void* k, const void* v, void* o, float* lse, int S, int BH, float c,
+               hipStream_t stream) {
     const int n_qblk = (S + Cfg::BM - 1) / Cfg::BM;
     const int64_t grid = (int64_t)n_qblk * BH;
     if (grid > (int64_t)1 << 24) return FA_ERR_TOO_LARGE;
@@ -47,6 +53,17 @@ int launch_mfma(const void* q, const void* k, const void* v, void* o, float* lse
                        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse,
                        S, BH, n_qblk, c);
     return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+template <typename T, int D, bool CAUSAL>
+int launch_mfma(const void* q, const void* k, const void* v, void* o, float* lse, int S, int BH,
+                float c, hipStream_t stream) {
+    using TL = Tiles<D>;
+    using Large = MfmaConfig<D, CAUSAL, TL::QB, TL::NW, TL::BN>;
+    using Small = MfmaConfig<D, CAUSAL, TL::SMALL_QB, TL::SMALL_NW, TL::BN>;
+    const int64_t large_grid = (int64_t)((S + Large::BM - 1) / Large::BM) * BH;
+    if (large_grid >= kFullGrid) return launch_cfg<T, Large>(q, k, v, o, lse, S, BH, c, stream);
+    return launch_cfg<T, Small>(q, k, v, o, lse, S, BH, c, stream);
 }
 
 template <int D, bool CAUSAL>
@@ -93,7 +110,11 @@ extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, floa
     if (D != 16 && D != 32 && D != 64 && D != 128) return FA_ERR_HEAD_DIM;
     if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
     if (causal != 0 && causal != 1) return FA_ERR_CAUSAL;
-    if (!isfinite(scale) || !(scale > 0.f)) return FA_ERR_SCALE;
+    // finite and > 0, tested on the bits (the library is built without NaN semantics)
+    uint32_t sbits;
+    memcpy(&sbits, &scale, sizeof sbits);
+    if (((sbits >> 23) & 0xFFu) == 0xFFu || (sbits >> 31) != 0u || (sbits & 0x7FFFFFFFu) == 0u)
+        return FA_ERR_SCALE;
     if (B == 0 || H == 0 || S == 0) return FA_OK;  // empty problem: nothing to compute
     if (!q || !k || !v || !o || !lse) return FA_ERR_NULL_POINTER;
     // index ranges: heads*S must fit the kernels' int arithmetic, S*D per head int64
