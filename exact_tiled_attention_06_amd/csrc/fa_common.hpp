@@ -80,4 +80,10 @@ __device__ __forceinline__ float halves_sum(float x) {
     return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
 }
 
+// Make a loaded value opaque to the optimiser, so that it stays in registers
+// rather than being re-loaded from memory later when registers are scarce.
+__device__ __forceinline__ void pin(u32x4& v) {
+    asm volatile("" : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]));
+}
+
 }  // namespace fa

@@ -7,8 +7,8 @@
 // Each wave owns 32 * QB whole query rows, so no softmax statistics cross a
 // wave ("Inside FlashAttention", section 4.3, split-Q).
 //
-// Per wave and key tile:
-//   S^T = K_tile * Q^T        32x32x16 MFMAs, fp32 accumulators.  Computing the
+// Work per wave and key tile t:
+//   S^T = K_t * Q^T           32x32x16 MFMAs, fp32 accumulators.  Computing the
 //                             transpose puts one query per lane column, so a row
 //                             maximum or sum is a reduction inside the lane plus
 //                             one exchange between the two wave halves.
@@ -16,32 +16,47 @@
 //                             end of the sequence; off-band tiles take no compare
 //                             ("Triton 实现", section "Causal Mask 的处理";
 //                             "T5 讲解", section ⑤).
-//   online softmax            exp2 form with c = scale * log2(e) ("Triton 实现",
-//                             section "内层循环"): the tile's row maximum m_t = c *
-//                             rowmax(S); when m_t exceeds the running reference
-//                             m by more than TAU (log2 units) for any row of the
-//                             wave, every row moves to m_new = max(m, m_t) and
-//                             rescales l and acc by alpha = exp2(m - m_new)
-//                             ("从零训练语言模型（第二部分）", section "安全 / 在线
-//                             softmax"); p = exp2(S*c - m), l += rowsum(p).
-//                             Keeping m until the maximum has grown by TAU leaves
-//                             every p <= 2^TAU, far inside fp16 / bf16 / fp32
-//                             range, and saves the rescale on almost every tile.
-//   O^T += V^T * P^T          P rounded (nearest-even) to the input type,
-//                             fp32 accumulation.
+//   online softmax            exp2 form, c = scale * log2(e) ("Triton 实现",
+//                             section "内层循环"): p = exp2(S*c - m), l += rowsum(p),
+//                             P rounded (nearest-even) to the input type.
+//   O^T += V_t^T * P^T        fp32 accumulation.
 // The epilogue divides by l once and writes O and lse = ln2 * (m + log2 l), the
 // natural-log form ("Inside FlashAttention", sections 2.4 and 4.1).
 //
+// The running reference m.  The pages move m to the running row maximum on
+// every tile and rescale l and acc by alpha = exp(m_old - m_new)
+// ("从零训练语言模型（第二部分）", section "安全 / 在线 softmax").  Here m moves
+// only when it must: each tile is first exponentiated against the current m;
+// if any of the wave's partial row sums of that tile exceeds 2^14 (so some
+// p > 2^14, or an exp2 overflowed), the tile is redone the pages' way -- m_new =
+// max(m, c * rowmax(S)), l and acc rescaled by alpha = exp2(m - m_new), p
+// recomputed.  Every accepted p is <= 2^14, inside fp16 range, and the result
+// is the same exact attention; on typical inputs only the first tile of a row
+// takes the slow path, which removes the per-element maximum from all others.
+//
+// Two loop shapes (Cfg::PIPE).  Pipelined: within one wave the MFMAs of a tile
+// depend on that tile's softmax and the other way round, so iteration t issues,
+// as one straight-line block, the S MFMAs of tile t+1 and the P*V MFMAs of tile
+// t-1 together with the softmax of tile t; the matrix cores then work on the
+// neighbouring tiles while the vector ALUs run the exponentials.  This needs two
+// sets of score and P registers.  Plain: one tile after the other (S, mask,
+// softmax, P*V) with one register set, and an LDS tile of TBN keys consumed in
+// TBN / BN compute steps between barriers; used where the accumulators leave no
+// room for a second set (D = 128), with the other waves of the SIMD providing
+// the overlap.
+//
 // Data movement: Q fragments live in VGPRs for the whole loop ("T5 讲解",
 // section ③).  K and V tiles go from HBM straight into LDS with 16-byte
-// global_load_lds transfers (no VGPR staging), double-buffered in separately
-// declared LDS arrays: tile t+1 is in flight while tile t is consumed, and one
-// barrier per tile publishes it.  Both tiles are stored row-major with an XOR
-// swizzle of 16-byte chunks per row (applied on the HBM side of the transfer),
-// chosen so that the K operand reads (ds_read_b128, one 16-byte chunk of 32
-// consecutive rows) and the V operand reads (ds_read_b64_tr_b16, 8-byte pieces
-// of four consecutive rows, transposed across lanes) hit distinct banks.
+// global_load_lds transfers (no VGPR staging), two buffers each in separately
+// declared LDS arrays (so the compiler's LDS-DMA tracking sees them apart); in
+// the pipelined loop K runs one tile ahead of V.  Both are stored row-major with an XOR swizzle of
+// 16-byte chunks per row (applied on the HBM side of the transfer), chosen so
+// that the K operand reads (ds_read_b128 of one chunk of 32 consecutive rows)
+// and the V operand reads (ds_read_b64_tr_b16 of 8-byte pieces of four
+// consecutive rows, transposed across lanes) hit distinct banks.
 #pragma once
+
+#include <type_traits>
 
 #include "fa_common.hpp"
 
@@ -51,8 +66,11 @@ namespace fa {
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-template <int D_, bool CAUSAL_, int QB_, int NW_, int BN_>
+template <int D_, bool CAUSAL_, int QB_, int NW_, int BN_, bool PIPE_ = true, int OCC_ = 2, int TBN_ = BN_>
 struct MfmaConfig {
+    static constexpr int TBN = TBN_;        // keys per LDS tile (a multiple of BN; BN = keys per compute step)
+    static constexpr bool PIPE = PIPE_;     // software-pipelined tile loop (two score/P sets)
+    static constexpr int OCC = OCC_;        // waves per SIMD the register budget is sized for
     static constexpr int D = D_;
     static constexpr bool CAUSAL = CAUSAL_;
     static constexpr int QB = QB_;          // 32-query column blocks per wave
@@ -66,19 +84,20 @@ struct MfmaConfig {
     static constexpr int DB = (D + 31) / 32;  // 32-row blocks of O^T
     static constexpr int RB = 2 * D;        // bytes per K / V row
     static constexpr int CPR = D / 8;       // 16-byte chunks per row
-    static constexpr int TILE = BN * RB;    // bytes per K or V tile
+    static constexpr int TILE = TBN * RB;   // bytes per K or V LDS tile
     static constexpr int LOADS = TILE / 1024;            // 1 KiB wave transfers per tile
-    static constexpr int LOADS_PER_WAVE = LOADS / NW;
+    static constexpr int LOADS_PER_WAVE = (LOADS + NW - 1) / NW;
     static_assert(D == 16 || D == 32 || D == 64 || D == 128, "head dim");
     static_assert(BN % 32 == 0, "BN must be a multiple of 32");
-    static_assert(LOADS % NW == 0 && LOADS_PER_WAVE >= 1, "tile transfers must split evenly over waves");
+    static_assert(TBN % BN == 0 && (PIPE_ ? TBN == BN : true), "LDS tile = whole compute steps");
+    static_assert(TILE % 1024 == 0 && (LOADS % NW == 0 || LOADS < NW), "tile transfers per wave");
     static_assert(2 * 2 * TILE <= 160 * 1024, "LDS");
 };
 
-// Rescale threshold (log2 units): p = exp2(S*c - m) stays <= 2^TAU.
-constexpr float kTau = 8.0f;
-// Initial running reference: finite and far below any score, so that
-// exp2(m_init - m_new) underflows to exactly 0 and no inf - inf arises.
+// A tile's partial row sums above this trigger the exact rescale path.
+constexpr float kSumLimit = 16384.0f;
+// Initial running reference: finite and far below any score, so that the first
+// tile always takes the rescale path and exp2(m_init - m_new) is exactly 0.
 constexpr float kMInit = -1.0e30f;
 
 // XOR swizzle of the 16-byte chunk index within a K row: one chunk read by 16
@@ -101,7 +120,7 @@ __device__ __forceinline__ int swz_v(int row) {
 __device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Issue this wave's share of the HBM -> LDS transfers of one K or V tile
-// (rows k0 .. k0+BN-1 of head `src`).  Rows at or beyond S repeat row S-1:
+// (rows k0 .. k0+TBN-1 of head `src`).  Rows at or beyond S repeat row S-1:
 // their keys are masked to -inf, so their finite values only ever meet p = 0.
 template <typename Cfg, bool ISV>
 __device__ __forceinline__ void load_tile(FA_LDS char* dst, const uint16_t* __restrict__ src, int k0, int S,
@@ -109,7 +128,8 @@ __device__ __forceinline__ void load_tile(FA_LDS char* dst, const uint16_t* __re
     constexpr int D = Cfg::D;
 #pragma unroll
     for (int i = 0; i < Cfg::LOADS_PER_WAVE; ++i) {
-        const int inst = wave * Cfg::LOADS_PER_WAVE + i;
+        const int inst = wave + i * Cfg::NW;
+        if (Cfg::LOADS < Cfg::NW && inst >= Cfg::LOADS) break;  // wave-uniform
         const int slot = inst * 64 + lane;
         const int row = slot / Cfg::CPR;
         const int p = slot % Cfg::CPR;
@@ -120,11 +140,139 @@ __device__ __forceinline__ void load_tile(FA_LDS char* dst, const uint16_t* __re
     }
 }
 
+// Per-wave state and the three pieces of work on one tile.
 template <typename T, typename Cfg>
-__global__ __attribute__((amdgpu_flat_work_group_size(Cfg::NT, Cfg::NT), amdgpu_waves_per_eu(2)))
+struct WaveTile {
+    static constexpr int D = Cfg::D, QB = Cfg::QB, KB = Cfg::KB, KS = Cfg::KS, DB = Cfg::DB;
+    static constexpr int RB = Cfg::RB;
+
+    // S^T = K Q^T for the tile in `kt`: A operand K[32kb + n][16ks + 8h .. +7].
+    static __device__ __forceinline__ void qk(const FA_LDS char* kt, const int (&offk)[KS],
+                                              const u32x4 (&qf)[QB][KS], f32x16 (&s)[QB][KB]) {
+        const f32x16 zero = {};
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const u32x4 kf = *reinterpret_cast<const FA_LDS u32x4*>(kt + kb * 32 * RB + offk[ks]);
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb)
+                    s[qb][kb] = mfma32x32x16<T>(kf, qf[qb][ks], ks == 0 ? zero : s[qb][kb]);
+            }
+    }
+
+    // O^T += V^T P^T for the tile in `vt`: A operand V[keys 32kb + 16j +
+    // {4h..4h+3, 8+4h..8+4h+3}][dim 32db + n] via two transposed 8-byte reads.
+    static __device__ __forceinline__ void pv(const FA_LDS char* vt, const int (&offv)[DB],
+                                              const u32x4 (&pk)[QB][KB][2], f32x16 (&oacc)[QB][DB]) {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int db = 0; db < DB; ++db) {
+                    const FA_LDS char* base = vt + (kb * 32 + 16 * j) * RB + offv[db];
+                    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS s16x4*)base);
+                    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS s16x4*)(base + 8 * RB));
+                    const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
+                    const u32x4 vf = {lo2[0], lo2[1], hi2[0], hi2[1]};
+#pragma unroll
+                    for (int qb = 0; qb < QB; ++qb)
+                        oacc[qb][db] = mfma32x32x16<T>(vf, pk[qb][kb][j], oacc[qb][db]);
+                }
+    }
+
+    // Causal / sequence-end mask: key of register r of block kb is
+    // k0 + 32kb + 4h + 8(r/4) + r%4; it is visible iff key <= last[qb].
+    static __device__ __forceinline__ void mask(f32x16 (&s)[QB][KB], const int (&last)[QB], int k0, int h) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                const int lim = last[qb] - (k0 + kb * 32 + 4 * h);
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    if (8 * (r >> 2) + (r & 3) > lim) s[qb][kb][r] = kNegInf;
+            }
+    }
+
+    // p = exp2(S*c - m): packs P for the P*V MFMAs (slot i of MFMA j holds
+    // register 8j + i) and returns the lane's partial row sums in rs.
+    static __device__ __forceinline__ void expo(const f32x16 (&s)[QB][KB], const float (&m_run)[QB], float c,
+                                                u32x4 (&pk)[QB][KB][2], float (&rs)[QB]) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            const float neg_m = -m_run[qb];
+            float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; r += 4) {
+                    const float p0 = exp2_fast(__builtin_fmaf(s[qb][kb][r + 0], c, neg_m));
+                    const float p1 = exp2_fast(__builtin_fmaf(s[qb][kb][r + 1], c, neg_m));
+                    const float p2 = exp2_fast(__builtin_fmaf(s[qb][kb][r + 2], c, neg_m));
+                    const float p3 = exp2_fast(__builtin_fmaf(s[qb][kb][r + 3], c, neg_m));
+                    a0 += p0 + p1;
+                    a1 += p2 + p3;
+                    const int j = r >> 3, w = (r & 7) >> 1;
+                    pk[qb][kb][j][w] = pack2<T>(p0, p1);
+                    pk[qb][kb][j][w + 1] = pack2<T>(p2, p3);
+                }
+            rs[qb] = a0 + a1;
+        }
+        // Materialise P here: otherwise the packing sinks below the rescale
+        // branch and keeps every unpacked fp32 p alive across it.
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                pin(pk[qb][kb][0]);
+                pin(pk[qb][kb][1]);
+            }
+    }
+
+    // True when some lane's partial sum of this tile is out of range (or NaN-free inf).
+    static __device__ __forceinline__ bool needs_rescale(const float (&rs)[QB]) {
+        bool bad = false;
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) bad |= !(rs[qb] <= kSumLimit);
+        return __builtin_amdgcn_ballot_w64(bad) != 0;
+    }
+
+    // The exact path: move m to max(m, c * rowmax(S)), rescale l and acc by
+    // alpha = exp2(m_old - m_new), and exponentiate the tile again.
+    static __device__ __forceinline__ void rescale(const f32x16 (&s)[QB][KB], float (&m_run)[QB], float (&l_run)[QB],
+                                                   f32x16 (&oacc)[QB][DB], float c, u32x4 (&pk)[QB][KB][2],
+                                                   float (&rs)[QB]) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            float a = s[qb][0][0], b = s[qb][0][1];
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int r = (kb == 0 ? 2 : 0); r < 16; r += 4) {
+                    a = fmaxf(fmaxf(a, s[qb][kb][r]), s[qb][kb][r + 1]);
+                    b = fmaxf(fmaxf(b, s[qb][kb][r + 2]), s[qb][kb][r + 3]);
+                }
+            const float m_new = fmaxf(m_run[qb], halves_max(fmaxf(a, b)) * c);
+            const float alpha = exp2_fast(m_run[qb] - m_new);
+            m_run[qb] = m_new;
+            l_run[qb] *= alpha;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[qb][db][r] *= alpha;
+        }
+        expo(s, m_run, c, pk, rs);
+    }
+};
+
+template <typename T, typename Cfg>
+__global__ __attribute__((amdgpu_flat_work_group_size(Cfg::NT, Cfg::NT), amdgpu_waves_per_eu(Cfg::OCC, Cfg::OCC)))
 void fa_fwd_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                         const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
                         int S, int BH, int n_qblk, float c) {
+    using W = WaveTile<T, Cfg>;
     constexpr int D = Cfg::D, QB = Cfg::QB, KB = Cfg::KB, KS = Cfg::KS, DB = Cfg::DB;
     constexpr int BN = Cfg::BN, BM = Cfg::BM, BMW = Cfg::BMW, RB = Cfg::RB;
     constexpr bool CAUSAL = Cfg::CAUSAL;
@@ -133,6 +281,8 @@ void fa_fwd_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
     __shared__ __attribute__((aligned(1024))) char k_lds1[Cfg::TILE];
     __shared__ __attribute__((aligned(1024))) char v_lds0[Cfg::TILE];
     __shared__ __attribute__((aligned(1024))) char v_lds1[Cfg::TILE];
+    FA_LDS char* const kbuf[2] = {(FA_LDS char*)k_lds0, (FA_LDS char*)k_lds1};
+    FA_LDS char* const vbuf[2] = {(FA_LDS char*)v_lds0, (FA_LDS char*)v_lds1};
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -157,24 +307,38 @@ void fa_fwd_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
 
     const int kend = CAUSAL ? min(q0 + BM, S) : S;
     const int ntiles = (kend + BN - 1) / BN;
+    // tiles this wave attends to (its last query's diagonal for causal)
+    const int wend = CAUSAL ? min(qw + BMW, S) : S;
+    const int wtiles = qw < S ? min(ntiles, (wend + BN - 1) / BN) : 0;
 
-    // Tile 0 in flight before anything else.
-    load_tile<Cfg, false>((FA_LDS char*)k_lds0, kh, 0, S, wave, lane);
-    load_tile<Cfg, true>((FA_LDS char*)v_lds0, vh, 0, S, wave, lane);
+    // First tiles in flight before anything else: K(0) and, pipelined, K(1);
+    // otherwise K(0) and V(0).
+    load_tile<Cfg, false>(kbuf[0], kh, 0, S, wave, lane);
+    if constexpr (Cfg::PIPE) {
+        if (ntiles > 1) load_tile<Cfg, false>(kbuf[1], kh, BN, S, wave, lane);
+    } else {
+        load_tile<Cfg, true>(vbuf[0], vh, 0, S, wave, lane);
+    }
 
     // Q^T operand fragments: lane holds Q[query][16ks + 8h .. +7].  Rows beyond
     // S repeat row S-1; their outputs are never stored.
     u32x4 qf[QB][KS];
+    int last[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         const int qrow = min(qw + qb * 32 + n, S - 1);
+        last[qb] = CAUSAL ? qrow : S - 1;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
             qf[qb][ks] = *reinterpret_cast<const u32x4*>(qh + (int64_t)qrow * D + ks * 16 + h * 8);
     }
+    // Q stays resident for the whole loop: read once ("T5 讲解", section ③)
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) pin(qf[qb][ks]);
 
     // Per-lane LDS byte offsets of the operand reads (constant over tiles).
-    // K: row n of each 32-key block, logical chunk 2ks + h.
     int offk[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) offk[ks] = n * RB + (((2 * ks + h) ^ swz_k<D>(n)) * 16);
@@ -202,127 +366,111 @@ void fa_fwd_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
 #pragma unroll
             for (int r = 0; r < 16; ++r) oacc[qb][db][r] = 0.f;
     }
-    const f32x16 zero = {};
 
-    auto step = [&](int t, FA_LDS char* kcur, FA_LDS char* vcur, FA_LDS char* knext, FA_LDS char* vnext) {
-        const int k0 = t * BN;
+    // Two sets of score and probability registers trade roles every tile.
+    f32x16 sA[QB][KB], sB[QB][KB];
+    u32x4 pA[QB][KB][2], pB[QB][KB][2];
+
+    if constexpr (Cfg::PIPE) {
         wait_vmcnt0();
         __syncthreads();
-        if (t + 1 < ntiles) {
-            load_tile<Cfg, false>(knext, kh, k0 + BN, S, wave, lane);
-            load_tile<Cfg, true>(vnext, vh, k0 + BN, S, wave, lane);
-        }
-        // A wave whose last query precedes the tile's first key has nothing to do here.
-        if (CAUSAL && k0 > qw + BMW - 1) return;
+        if (wtiles > 0) W::qk(kbuf[0], offk, qf, sA);
+    }
 
-        // ---- S^T = K Q^T --------------------------------------------------------
-        f32x16 s[QB][KB];
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const u32x4 kf = *reinterpret_cast<const FA_LDS u32x4*>(kcur + kb * 32 * RB + offk[ks]);
-#pragma unroll
-                for (int qb = 0; qb < QB; ++qb)
-                    s[qb][kb] = mfma32x32x16<T>(kf, qf[qb][ks], ks == 0 ? zero : s[qb][kb]);
-            }
-        }
+    // Iteration t: S(t) in s_cur, S(t+1) goes to s_nxt, P(t-1) in p_prv, P(t)
+    // goes to p_cur; K(t) / V(t) live in buffer t&1, K(t+1) / V(t-1) in the other.
+    // STEADY iterations (1 <= t, t+1 < wtiles, tile t unmasked) are branch-free
+    // so that their MFMAs and exponentials form one basic block.
+    auto iter = [&](auto steady, int t, FA_LDS char* kc, FA_LDS char* kn, FA_LDS char* vc, FA_LDS char* vp,
+                    f32x16 (&s_cur)[QB][KB], f32x16 (&s_nxt)[QB][KB], u32x4 (&p_prv)[QB][KB][2],
+                    u32x4 (&p_cur)[QB][KB][2]) {
+        constexpr bool STEADY = decltype(steady)::value;
+        const int k0 = t * BN;
+        wait_vmcnt0();
+        __syncthreads();  // K(t+1) and V(t-1) visible; K(t) and V(t-2) no longer read
+        // (a transfer past the last tile only re-reads clamped rows into a free buffer)
+        if (STEADY || t + 2 < ntiles) load_tile<Cfg, false>(kc, kh, k0 + 2 * BN, S, wave, lane);
+        load_tile<Cfg, true>(vc, vh, k0, S, wave, lane);
 
-        // ---- mask: only tiles that cross the diagonal or the end of the sequence --
-        if ((CAUSAL && k0 + BN - 1 > qw) || k0 + BN > S) {
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-                const int last = CAUSAL ? min(qw + qb * 32 + n, S - 1) : S - 1;
-#pragma unroll
-                for (int kb = 0; kb < KB; ++kb) {
-                    // key of register r = k0 + 32kb + 4h + 8(r/4) + r%4; visible iff key <= last
-                    const int lim = last - (k0 + kb * 32 + 4 * h);
-#pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        if (8 * (r >> 2) + (r & 3) > lim) s[qb][kb][r] = kNegInf;
-                }
+        float rs[QB];
+        if constexpr (STEADY) {
+            W::qk(kn, offk, qf, s_nxt);
+            W::pv(vp, offv, p_prv, oacc);
+            W::expo(s_cur, m_run, c, p_cur, rs);
+        } else {
+            const bool do_qk = t + 1 < wtiles;
+            const bool do_pv = t >= 1 && t <= wtiles;
+            if (t >= wtiles) {
+                if (do_pv) W::pv(vp, offv, p_prv, oacc);  // this wave's last tile, while V(t-1) is resident
+                return;
             }
+            if (do_qk) W::qk(kn, offk, qf, s_nxt);
+            if (do_pv) W::pv(vp, offv, p_prv, oacc);
+            if ((CAUSAL && k0 + BN - 1 > qw) || k0 + BN > S) W::mask(s_cur, last, k0, h);
+            W::expo(s_cur, m_run, c, p_cur, rs);
         }
-
-        // ---- online softmax --------------------------------------------------------
-        bool grow = false;
-        float m_tile[QB];
+        // P*V of tile t-1 is in acc now, so a rescale covers every earlier term.
+        if (W::needs_rescale(rs)) W::rescale(s_cur, m_run, l_run, oacc, c, p_cur, rs);
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-            float a = s[qb][0][0], b = s[qb][0][1];
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                for (int r = (kb == 0 ? 2 : 0); r < 16; r += 4) {
-                    a = fmaxf(fmaxf(a, s[qb][kb][r]), s[qb][kb][r + 1]);
-                    b = fmaxf(fmaxf(b, s[qb][kb][r + 2]), s[qb][kb][r + 3]);
-                }
-            m_tile[qb] = halves_max(fmaxf(a, b)) * c;
-            grow |= m_tile[qb] > m_run[qb] + kTau;
-        }
-        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-                const float m_new = fmaxf(m_run[qb], m_tile[qb]);
-                const float alpha = exp2_fast(m_run[qb] - m_new);
-                m_run[qb] = m_new;
-                l_run[qb] *= alpha;
-#pragma unroll
-                for (int db = 0; db < DB; ++db)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) oacc[qb][db][r] *= alpha;
-            }
-        }
-
-        u32x4 pk[QB][KB][2];
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-            const float neg_m = -m_run[qb];
-            float rs0 = 0.f, rs1 = 0.f;
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-                for (int r = 0; r < 16; r += 4) {
-                    const float p0 = exp2_fast(__builtin_fmaf(s[qb][kb][r + 0], c, neg_m));
-                    const float p1 = exp2_fast(__builtin_fmaf(s[qb][kb][r + 1], c, neg_m));
-                    const float p2 = exp2_fast(__builtin_fmaf(s[qb][kb][r + 2], c, neg_m));
-                    const float p3 = exp2_fast(__builtin_fmaf(s[qb][kb][r + 3], c, neg_m));
-                    rs0 += p0 + p1;
-                    rs1 += p2 + p3;
-                    // B operand of P*V: slot i of MFMA j holds register 8j + i
-                    const int j = r >> 3, w = (r & 7) >> 1;
-                    pk[qb][kb][j][w] = pack2<T>(p0, p1);
-                    pk[qb][kb][j][w + 1] = pack2<T>(p2, p3);
-                }
-            }
-            l_run[qb] += rs0 + rs1;
-        }
-
-        // ---- O^T += V^T P^T ---------------------------------------------------------
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-#pragma unroll
-                for (int db = 0; db < DB; ++db) {
-                    // A operand: V[keys 32kb + 16j + {4h..4h+3, 8+4h..8+4h+3}][dim 32db + n]
-                    FA_LDS char* base = vcur + (kb * 32 + 16 * j) * RB + offv[db];
-                    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS s16x4*)base);
-                    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS s16x4*)(base + 8 * RB));
-                    const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
-                    const u32x4 vf = {lo2[0], lo2[1], hi2[0], hi2[1]};
-#pragma unroll
-                    for (int qb = 0; qb < QB; ++qb)
-                        oacc[qb][db] = mfma32x32x16<T>(vf, pk[qb][kb][j], oacc[qb][db]);
-                }
-            }
-        }
+        for (int qb = 0; qb < QB; ++qb) l_run[qb] += rs[qb];
     };
+    using Steady = std::true_type;
+    using Edge = std::false_type;
 
-    for (int t = 0; t < ntiles; t += 2) {
-        step(t, (FA_LDS char*)k_lds0, (FA_LDS char*)v_lds0, (FA_LDS char*)k_lds1, (FA_LDS char*)v_lds1);
-        if (t + 1 < ntiles)
-            step(t + 1, (FA_LDS char*)k_lds1, (FA_LDS char*)v_lds1, (FA_LDS char*)k_lds0, (FA_LDS char*)v_lds0);
+    if constexpr (!Cfg::PIPE) {
+        // One LDS tile (TBN keys) per barrier; inside it, compute steps of BN
+        // keys: S, (mask), softmax, P*V -- single register sets.
+        constexpr int SUB = Cfg::TBN / BN;
+        const int nlds = (ntiles + SUB - 1) / SUB;
+        auto simple = [&](int lt, FA_LDS char* kc, FA_LDS char* vc, FA_LDS char* kn, FA_LDS char* vn)
+                          __attribute__((always_inline)) {
+            wait_vmcnt0();
+            __syncthreads();
+            if (lt + 1 < nlds) {
+                load_tile<Cfg, false>(kn, kh, (lt + 1) * Cfg::TBN, S, wave, lane);
+                load_tile<Cfg, true>(vn, vh, (lt + 1) * Cfg::TBN, S, wave, lane);
+            }
+#pragma unroll
+            for (int sub = 0; sub < SUB; ++sub) {
+                const int t = lt * SUB + sub;
+                if (t >= wtiles) break;  // wave-uniform
+                const int k0 = t * BN;
+                W::qk(kc + sub * BN * RB, offk, qf, sA);
+                if ((CAUSAL && k0 + BN - 1 > qw) || k0 + BN > S) W::mask(sA, last, k0, h);
+                float rs[QB];
+                W::expo(sA, m_run, c, pA, rs);
+                if (W::needs_rescale(rs)) W::rescale(sA, m_run, l_run, oacc, c, pA, rs);
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) l_run[qb] += rs[qb];
+                W::pv(vc + sub * BN * RB, offv, pA, oacc);
+            }
+        };
+        for (int lt = 0; lt < nlds; lt += 2) {
+            simple(lt, kbuf[0], vbuf[0], kbuf[1], vbuf[1]);
+            if (lt + 1 < nlds) simple(lt + 1, kbuf[1], vbuf[1], kbuf[0], vbuf[0]);
+        }
+    } else {
+    // leading tiles that need no mask for any of this wave's rows
+    const int unmasked = min(CAUSAL ? (qw + 1) / BN : ntiles, S / BN);
+    const int steady_end = min(wtiles - 1, unmasked);  // steady for 1 <= t < steady_end
+
+    iter(Edge{}, 0, kbuf[0], kbuf[1], vbuf[0], vbuf[1], sA, sB, pA, pB);
+    int t = 1;
+    for (; t + 1 < steady_end; t += 2) {
+        iter(Steady{}, t, kbuf[1], kbuf[0], vbuf[1], vbuf[0], sB, sA, pB, pA);
+        iter(Steady{}, t + 1, kbuf[0], kbuf[1], vbuf[0], vbuf[1], sA, sB, pA, pB);
+    }
+    for (; t < ntiles; t += 2) {
+        iter(Edge{}, t, kbuf[1], kbuf[0], vbuf[1], vbuf[0], sB, sA, pB, pA);
+        if (t + 1 < ntiles) iter(Edge{}, t + 1, kbuf[0], kbuf[1], vbuf[0], vbuf[1], sA, sB, pA, pB);
+    }
+    // drain: P*V of the last tile for waves that attend to every tile
+    wait_vmcnt0();
+    __syncthreads();
+    if (wtiles == ntiles && wtiles > 0) {
+        if ((ntiles - 1) & 1) W::pv(vbuf[1], offv, pA, oacc);
+        else W::pv(vbuf[0], offv, pB, oacc);
+    }
     }
 
     // ---- epilogue: O = acc / l, lse = ln2 * (m + log2 l) ---------------------------
