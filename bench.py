@@ -10,8 +10,11 @@ fraction of the MI355X dense fp16 matrix peak (2.5 PFLOP/s).
 Prints one JSON line.  Also reported:
   roofline      achieved TFLOP/s of the attention kernel from HIP events around
                 every timed launch on the stream it runs on, against the peak;
-                `traffic` is filled from rocprofv3 counters when given
-                (--traffic-bytes) and null otherwise;
+                `traffic` is the HBM bytes per launch measured with rocprofv3
+                FETCH_SIZE / WRITE_SIZE (scaled by a copy-kernel calibration),
+                taken from the committed summary in profiles/ for this workload
+                while the kernel sources still hash to what was profiled, else
+                null (--traffic-bytes overrides);
   cpu_baseline  the float64 CPU oracle timed on this host's cores over the
                 whole workload (every row of every head), in the same unit.
 
@@ -34,6 +37,24 @@ sys.path.insert(0, ROOT)
 
 PEAK_MFMA_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "f32": 157.3}  # dense, MI355X published
 PEAK_HBM_GBS = 8000.0
+
+
+def profiled_traffic(workload):
+    """HBM bytes per launch from profiles/*_traffic.txt for this workload, or
+    None when no summary matches the current kernel sources."""
+    import glob
+    from exact_tiled_attention_06_amd import build
+    want = build.source_hash()
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*_traffic.txt"))):
+        kv = {}
+        with open(path) as f:
+            for line in f:
+                if ":" in line and not line.startswith(" "):
+                    key, _, val = line.partition(":")
+                    kv[key.strip()] = val.strip()
+        if kv.get("workload") == workload and kv.get("source_sha256") == want:
+            return float(kv["traffic_bytes_per_launch"])
+    return None
 
 
 def time_workload(fa, torch, w, causal, steps, warmup):
@@ -88,7 +109,13 @@ def main():
     ap.add_argument("--traffic-bytes", type=float, default=None,
                     help="HBM bytes per launch measured with rocprofv3 counters")
     ap.add_argument("--sweep", default=None, help="write per-workload JSON lines to this file")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="instead of attention, run plain device-to-device copies of this many bytes "
+                         "(calibrates the FETCH_SIZE / WRITE_SIZE counters against a known byte count)")
     args = ap.parse_args()
+    if args.steps < 1 or args.warmup < 0:
+        print("bench.py: --steps must be >= 1 and --warmup >= 0", file=sys.stderr)
+        return 2
 
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} is not supported; this attention forward runs on one GPU "
@@ -103,6 +130,16 @@ def main():
         print("bench.py: no GPU visible", file=sys.stderr)
         return 1
 
+    if args.copy_bytes:
+        n = args.copy_bytes // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup + args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n * 4, "copies": args.warmup + args.steps}), flush=True)
+        return 0
+
     w = workloads.BY_NAME[args.workload]
     causal = w.causal[-1]
     wall, kernel_ms = time_workload(fa, torch, w, causal, args.steps, args.warmup)
@@ -112,6 +149,7 @@ def main():
     avg_kernel_ms = sum(kernel_ms) / len(kernel_ms)
     achieved = flops / (avg_kernel_ms * 1e-3) / 1e12
     peak = PEAK_MFMA_TFLOPS[w.dtype]
+    traffic = args.traffic_bytes if args.traffic_bytes is not None else profiled_traffic(w.name)
     out = {
         "metric": "attention fwd TFLOP/s and % of MI355X dense fp16/bf16 MFMA peak",
         "value": round(value, 2),
@@ -137,7 +175,9 @@ def main():
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
-            "traffic": args.traffic_bytes,
+            "traffic": traffic,
+            "traffic_unit": "bytes per launch (HBM, rocprofv3 FETCH_SIZE + WRITE_SIZE)",
+            "algorithmic_bytes": w.hbm_bytes(),
             "kernel_ms_avg": round(avg_kernel_ms, 5),
             "kernel_ms_min": round(min(kernel_ms), 5),
             "hbm_gbs_algorithmic": round(w.hbm_bytes() / (avg_kernel_ms * 1e-3) / 1e9, 1),

@@ -6,6 +6,7 @@ source tree.
 """
 from __future__ import annotations
 
+import hashlib
 import os
 import shutil
 import subprocess
@@ -53,6 +54,18 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{res.stderr[-8000:]}")
     os.replace(tmp, LIBRARY)
     return LIBRARY
+
+
+def source_hash() -> str:
+    """sha256 over every source and header the library is built from, plus the
+    compiler flags: a profile taken of one build is valid for another build
+    only when this matches."""
+    h = hashlib.sha256()
+    for f in SOURCES + HEADERS:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    h.update(" ".join(FLAGS).encode())
+    return h.hexdigest()
 
 
 def is_stale() -> bool:
