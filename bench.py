@@ -126,6 +126,8 @@ def main():
     import exact_tiled_attention_06_amd as fa
     import workloads
 
+    fa.library()  # fails loudly when libfa.so is missing
+
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         return 1

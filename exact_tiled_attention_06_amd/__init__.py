@@ -3,7 +3,9 @@
 Argument marshalling only: every step of the attention runs in the HIP kernels
 behind the C ABI declared in ``include/fa.h``.  PyTorch supplies device memory
 and the current stream; this module never computes attention itself and has no
-CPU fallback -- importing it fails loudly when the library is not built.
+CPU fallback -- the first call (or ``library()``) fails loudly when the library
+is not built.  The library is loaded on first use so that the build step can
+import this package before the library exists.
 
     fa_fwd(q, k, v, o, lse, B, H, S, D, causal, scale, dtype, stream)
         the C entry point with raw device pointers (ints) and sizes;
@@ -62,7 +64,16 @@ def _load() -> ctypes.CDLL:
     return lib
 
 
-_lib = _load()
+_lib: ctypes.CDLL | None = None
+
+
+def library() -> ctypes.CDLL:
+    """libfa.so, loaded on first use (so that the build step can import this
+    package before the library exists); raises ImportError when it is not built."""
+    global _lib
+    if _lib is None:
+        _lib = _load()
+    return _lib
 
 
 class FaError(RuntimeError):
@@ -78,13 +89,13 @@ class FaValueError(ValueError):
 
 
 def fa_status_string(status: int) -> str:
-    return _lib.fa_status_string(int(status)).decode()
+    return library().fa_status_string(int(status)).decode()
 
 
 def fa_fwd(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, S: int, D: int,
            causal: int, scale: float, dtype: int, stream: int) -> int:
     """The C entry point: raw device addresses and sizes; returns the status code."""
-    return int(_lib.fa_fwd(q, k, v, o, lse, B, H, S, D, int(causal), float(scale), int(dtype), stream))
+    return int(library().fa_fwd(q, k, v, o, lse, B, H, S, D, int(causal), float(scale), int(dtype), stream))
 
 
 def check(status: int) -> None:

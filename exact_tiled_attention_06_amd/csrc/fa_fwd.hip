@@ -14,6 +14,11 @@
 #include "../../include/fa.h"
 #include "fa_f32.hpp"
 #include "fa_mfma.hpp"
+#include "fa_split.hpp"
+
+#ifndef FA_SPLIT_TBN
+#define FA_SPLIT_TBN 128
+#endif
 
 namespace {
 
@@ -30,11 +35,16 @@ struct Tiles {
     static constexpr int NW = (D == 128) ? 8 : 4;
     static constexpr int BN = (D == 16 || D == 128) ? 64 : 32;
     static constexpr bool PIPE = (D != 128);
-    static constexpr int TBN = (D == 128) ? 128 : BN;
+    // keys per LDS tile (one barrier each): the two-column-block kernel stages
+    // 128 keys at D = 32; at D = 64 its registers leave no room for the longer
+    // unrolled steady loop, which spills, so it stages one 32-key tile
+    static constexpr int TBN = (D == 128) ? 128 : (D == 32 ? FA_SPLIT_TBN : BN);
     // small grids: 64 query rows per workgroup
     static constexpr int SMALL_QB = 1;
     static constexpr int SMALL_NW = 2;
     static constexpr int SMALL_BN = (D == 16) ? 64 : 32;
+    // D = 128 has no registers for the pipelined loop's second score/P set
+    static constexpr bool SMALL_PIPE = (D != 128);
 };
 
 // A grid of at least this many workgroups fills the machine twice over.
@@ -54,9 +64,14 @@ int launch_cfg(const void* q, const void* k, const void* v, void* o, float* lse,
     const int64_t grid = (int64_t)n_qblk * BH;
     if (grid > (int64_t)1 << 24) return FA_ERR_TOO_LARGE;
     (void)hipGetLastError();  // clear a stale error so the check below sees this launch only
-    hipLaunchKernelGGL((fa_fwd_mfma_kernel<T, Cfg>), dim3((unsigned)grid), dim3(Cfg::NT), 0, stream,
-                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse,
-                       S, BH, n_qblk, c);
+    if constexpr (Cfg::QB == 2 && Cfg::KB == 1 && Cfg::PIPE)
+        hipLaunchKernelGGL((fa_fwd_split_kernel<T, Cfg>), dim3((unsigned)grid), dim3(Cfg::NT), 0, stream,
+                           (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse,
+                           S, BH, n_qblk, c);
+    else
+        hipLaunchKernelGGL((fa_fwd_mfma_kernel<T, Cfg>), dim3((unsigned)grid), dim3(Cfg::NT), 0, stream,
+                           (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse,
+                           S, BH, n_qblk, c);
     return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
@@ -65,7 +80,7 @@ int launch_mfma(const void* q, const void* k, const void* v, void* o, float* lse
                 float c, hipStream_t stream) {
     using TL = Tiles<D>;
     using Large = MfmaConfig<D, CAUSAL, TL::QB, TL::NW, TL::BN, TL::PIPE, 2, TL::TBN>;
-    using Small = MfmaConfig<D, CAUSAL, TL::SMALL_QB, TL::SMALL_NW, TL::SMALL_BN>;
+    using Small = MfmaConfig<D, CAUSAL, TL::SMALL_QB, TL::SMALL_NW, TL::SMALL_BN, TL::SMALL_PIPE>;
     const int64_t large_grid = (int64_t)((S + Large::BM - 1) / Large::BM) * BH;
     if (large_grid >= kFullGrid) return launch_cfg<T, Large>(q, k, v, o, lse, S, BH, c, stream);
     return launch_cfg<T, Small>(q, k, v, o, lse, S, BH, c, stream);
@@ -127,6 +142,9 @@ extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, floa
     if (B > kMaxInt || H > kMaxInt || B * H > kMaxInt / 2 || S > (kMaxInt >> 1)) return FA_ERR_TOO_LARGE;
     const int64_t BH = B * H;
     if (BH > INT64_MAX / S || BH * S > INT64_MAX / (D * 8)) return FA_ERR_TOO_LARGE;
+    // the matrix-core kernels address one head's K or V rows through a buffer
+    // resource with a 32-bit extent: S * D * 2 bytes must stay below 2^31
+    if (dtype != FA_DTYPE_F32 && S * D * 2 > kMaxInt) return FA_ERR_TOO_LARGE;
     const int64_t tensor_bytes = BH * S * D * elem_size(dtype);
     const int64_t lse_bytes = BH * S * 4;
     if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15) return FA_ERR_ALIGNMENT;

@@ -89,7 +89,7 @@ struct MfmaConfig {
     static constexpr int LOADS_PER_WAVE = (LOADS + NW - 1) / NW;
     static_assert(D == 16 || D == 32 || D == 64 || D == 128, "head dim");
     static_assert(BN % 32 == 0, "BN must be a multiple of 32");
-    static_assert(TBN % BN == 0 && (PIPE_ ? TBN == BN : true), "LDS tile = whole compute steps");
+    static_assert(TBN % BN == 0, "LDS tile = whole compute steps");
     static_assert(TILE % 1024 == 0 && (LOADS % NW == 0 || LOADS < NW), "tile transfers per wave");
     static_assert(2 * 2 * TILE <= 160 * 1024, "LDS");
 };
@@ -119,34 +119,112 @@ __device__ __forceinline__ int swz_v(int row) {
 
 __device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-// Issue this wave's share of the HBM -> LDS transfers of one K or V tile
-// (rows k0 .. k0+TBN-1 of head `src`).  Rows at or beyond S repeat row S-1:
-// their keys are masked to -inf, so their finite values only ever meet p = 0.
+// Wait until at most n (0..8, wave-uniform) of this wave's vector-memory
+// operations are outstanding; s_waitcnt takes the count as an immediate.
+__device__ __forceinline__ void wait_vmcnt_le(int n) {
+    switch (n) {
+        case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+        case 1: __builtin_amdgcn_s_waitcnt(0x0F71); break;
+        case 2: __builtin_amdgcn_s_waitcnt(0x0F72); break;
+        case 3: __builtin_amdgcn_s_waitcnt(0x0F73); break;
+        case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
+        case 5: __builtin_amdgcn_s_waitcnt(0x0F75); break;
+        case 6: __builtin_amdgcn_s_waitcnt(0x0F76); break;
+        case 7: __builtin_amdgcn_s_waitcnt(0x0F77); break;
+        default: __builtin_amdgcn_s_waitcnt(0x0F78); break;
+    }
+}
+
+// Per-lane byte offset (within one head's K or V) of this wave's i-th 16-byte
+// transfer of a tile starting at key 0: transfer `inst` of the tile covers LDS
+// bytes inst*1024 .. +1023, lane l fills 16 bytes at l*16 of it, i.e. row
+// slot / CPR, chunk slot % CPR (slot = inst*64 + l); the chunk read from HBM is
+// that position's swizzled chunk.
 template <typename Cfg, bool ISV>
-__device__ __forceinline__ void load_tile(FA_LDS char* dst, const uint16_t* __restrict__ src, int k0, int S,
+__device__ __forceinline__ uint32_t tile_lane_offset(int inst, int lane) {
+    const int slot = inst * 64 + lane;
+    const int row = slot / Cfg::CPR;
+    const int p = slot % Cfg::CPR;
+    const int c = p ^ (ISV ? swz_v<Cfg::D>(row) : swz_k<Cfg::D>(row));
+    return (uint32_t)(row * Cfg::RB + c * 16);
+}
+
+// Buffer-resource word 3 for raw (untyped) dword buffer loads on gfx9-class
+// hardware: a non-zero data format, everything else default.
+constexpr int kBufferFlags = 0x00020000;
+
+// Buffer resource of one head's K or V rows (`bytes` long): transfers that
+// reach at or beyond its end read zeros.  (Templated on the element type, like
+// every helper that calls target builtins here, so that every kernel instance
+// has its own copy: the host-side pass of one instance cannot then poison the
+// overload for the next.)
+template <typename T>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const uint16_t* head, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc((void*)head, 0, bytes, kBufferFlags);
+}
+
+// Issue this wave's share of the HBM -> LDS transfers of one K or V tile (rows
+// k0 .. k0+TBN-1 of the head behind `rsrc`), as buffer loads that write LDS
+// directly; rows at or beyond S read as zeros (their keys are masked to -inf and
+// their values only ever meet p = 0).  Transfer i of the wave (inst = wave +
+// i*NW) covers rows i*NW*1024/RB further on than transfer 0; when that is a
+// multiple of the swizzles' 16-row period, its lane offsets are transfer 0's
+// (lane_off) plus i*NW KiB, so no per-transfer offset occupies a register.
+template <typename T, typename Cfg, bool ISV>
+__device__ __forceinline__ void load_tile(FA_LDS char* dst, __amdgpu_buffer_rsrc_t rsrc, uint32_t lane_off, int k0,
                                           int wave, int lane) {
-    constexpr int D = Cfg::D;
+    constexpr bool kPeriodic = (Cfg::NW * 1024 / Cfg::RB) % 16 == 0;
 #pragma unroll
     for (int i = 0; i < Cfg::LOADS_PER_WAVE; ++i) {
         const int inst = wave + i * Cfg::NW;
         if (Cfg::LOADS < Cfg::NW && inst >= Cfg::LOADS) break;  // wave-uniform
-        const int slot = inst * 64 + lane;
-        const int row = slot / Cfg::CPR;
-        const int p = slot % Cfg::CPR;
-        const int c = p ^ (ISV ? swz_v<D>(row) : swz_k<D>(row));
-        const int grow = min(k0 + row, S - 1);
-        const uint16_t* g = src + (int64_t)grow * D + c * 8;
-        __builtin_amdgcn_global_load_lds((const void*)g, (FA_LDS void*)(dst + inst * 1024), 16, 0, 0);
+        const uint32_t off = kPeriodic ? lane_off + (uint32_t)(i * Cfg::NW * 1024) : tile_lane_offset<Cfg, ISV>(inst, lane);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (FA_LDS void*)(dst + inst * 1024), 16,
+                                                 off + (uint32_t)(k0 * Cfg::RB), 0, 0, 0);
     }
 }
 
-// Per-wave state and the three pieces of work on one tile.
+// One row-sum step for a pair (p0, p1) of a lane's probabilities: two fp32 adds
+// of the unrounded values (the pages sum p before it is rounded for the P*V
+// product).  Every path sums the pairs of a tile in the same order, so a row's l
+// does not depend on which path (steady, edge, rescale) handled a tile.
+__device__ __forceinline__ float pair_sum(float acc, float p0, float p1, bool first) {
+    return first ? p0 + p1 : acc + (p0 + p1);
+}
+
+// One 1 KiB HBM -> LDS transfer (64 lanes x 16 bytes): the lane's 16 bytes at
+// lane_off + k0 * RB of the head behind `rsrc` to dst + lane * 16.
+template <typename T, typename Cfg>
+__device__ __forceinline__ void load_part(FA_LDS char* dst, __amdgpu_buffer_rsrc_t rsrc, uint32_t lane_off, int k0) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (FA_LDS void*)dst, 16, lane_off + (uint32_t)(k0 * Cfg::RB), 0, 0, 0);
+}
+
+// Per-wave state and the pieces of work on one tile.
 template <typename T, typename Cfg>
 struct WaveTile {
     static constexpr int D = Cfg::D, QB = Cfg::QB, KB = Cfg::KB, KS = Cfg::KS, DB = Cfg::DB;
     static constexpr int RB = Cfg::RB;
+    static constexpr int NQK = KB * KS * QB;      // S^T MFMAs per tile
+    static constexpr int NPV = KB * 2 * DB * QB;  // O^T MFMAs per tile
+    static constexpr int NP = QB * KB * 8;        // score pairs per lane per tile
 
-    // S^T = K Q^T for the tile in `kt`: A operand K[32kb + n][16ks + 8h .. +7].
+    // K fragment of 32-key block kb, k-step ks: A operand K[32kb + n][16ks + 8h .. +7].
+    static __device__ __forceinline__ u32x4 k_frag(const FA_LDS char* kt, const int (&offk)[KS], int kb, int ks) {
+        return *reinterpret_cast<const FA_LDS u32x4*>(kt + kb * 32 * RB + offk[ks]);
+    }
+
+    // V^T fragment of keys 32kb + 16j + {4h..4h+3, 8+4h..8+4h+3}, dims 32db + n,
+    // via two transposed 8-byte reads.
+    static __device__ __forceinline__ u32x4 v_frag(const FA_LDS char* vt, const int (&offv)[DB], int kb, int j,
+                                                   int db) {
+        const FA_LDS char* base = vt + (kb * 32 + 16 * j) * RB + offv[db];
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS s16x4*)base);
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS s16x4*)(base + 8 * RB));
+        const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
+        return u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
+    }
+
+    // S^T = K Q^T for the tile in `kt`.
     static __device__ __forceinline__ void qk(const FA_LDS char* kt, const int (&offk)[KS],
                                               const u32x4 (&qf)[QB][KS], f32x16 (&s)[QB][KB]) {
         const f32x16 zero = {};
@@ -154,15 +232,14 @@ struct WaveTile {
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                const u32x4 kf = *reinterpret_cast<const FA_LDS u32x4*>(kt + kb * 32 * RB + offk[ks]);
+                const u32x4 kf = k_frag(kt, offk, kb, ks);
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb)
                     s[qb][kb] = mfma32x32x16<T>(kf, qf[qb][ks], ks == 0 ? zero : s[qb][kb]);
             }
     }
 
-    // O^T += V^T P^T for the tile in `vt`: A operand V[keys 32kb + 16j +
-    // {4h..4h+3, 8+4h..8+4h+3}][dim 32db + n] via two transposed 8-byte reads.
+    // O^T += V^T P^T for the tile in `vt`.
     static __device__ __forceinline__ void pv(const FA_LDS char* vt, const int (&offv)[DB],
                                               const u32x4 (&pk)[QB][KB][2], f32x16 (&oacc)[QB][DB]) {
 #pragma unroll
@@ -171,11 +248,7 @@ struct WaveTile {
             for (int j = 0; j < 2; ++j)
 #pragma unroll
                 for (int db = 0; db < DB; ++db) {
-                    const FA_LDS char* base = vt + (kb * 32 + 16 * j) * RB + offv[db];
-                    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS s16x4*)base);
-                    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS s16x4*)(base + 8 * RB));
-                    const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
-                    const u32x4 vf = {lo2[0], lo2[1], hi2[0], hi2[1]};
+                    const u32x4 vf = v_frag(vt, offv, kb, j, db);
 #pragma unroll
                     for (int qb = 0; qb < QB; ++qb)
                         oacc[qb][db] = mfma32x32x16<T>(vf, pk[qb][kb][j], oacc[qb][db]);
@@ -196,30 +269,31 @@ struct WaveTile {
             }
     }
 
-    // p = exp2(S*c - m): packs P for the P*V MFMAs (slot i of MFMA j holds
-    // register 8j + i) and returns the lane's partial row sums in rs.
+    // Pair e of the lane's scores: column block qb = e / (8 KB), key block
+    // kb = (e / 8) % KB, registers r = 2 (e % 8) and r + 1.  Its packed P lands in
+    // slot (e % 8) % 4 of MFMA operand (e % 8) / 4 (operand j holds registers
+    // 8j .. 8j+7, i.e. keys 16j + {4h..4h+3, 8+4h..8+4h+3} of the block).
+    struct Pair {
+        float p0, p1;
+    };
+    static __device__ __forceinline__ Pair pair_exp(const f32x16 (&s)[QB][KB], const float (&m_run)[QB], float c,
+                                                    int e) {
+        const int qb = e / (8 * KB), kb = (e / 8) % KB, r = 2 * (e % 8);
+        return {exp2_fast(__builtin_fmaf(s[qb][kb][r], c, -m_run[qb])),
+                exp2_fast(__builtin_fmaf(s[qb][kb][r + 1], c, -m_run[qb]))};
+    }
+    static __device__ __forceinline__ void pair_pack(Pair x, int e, u32x4 (&pk)[QB][KB][2], float (&rs)[QB]) {
+        const int qb = e / (8 * KB), kb = (e / 8) % KB, i = e % 8;
+        pk[qb][kb][i >> 2][i & 3] = pack2<T>(x.p0, x.p1);
+        rs[qb] = pair_sum(rs[qb], x.p0, x.p1, kb == 0 && i == 0);
+    }
+
+    // p = exp2(S*c - m): packs P for the P*V MFMAs and returns the lane's
+    // partial row sums in rs.
     static __device__ __forceinline__ void expo(const f32x16 (&s)[QB][KB], const float (&m_run)[QB], float c,
                                                 u32x4 (&pk)[QB][KB][2], float (&rs)[QB]) {
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-            const float neg_m = -m_run[qb];
-            float a0 = 0.f, a1 = 0.f;
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; r += 4) {
-                    const float p0 = exp2_fast(__builtin_fmaf(s[qb][kb][r + 0], c, neg_m));
-                    const float p1 = exp2_fast(__builtin_fmaf(s[qb][kb][r + 1], c, neg_m));
-                    const float p2 = exp2_fast(__builtin_fmaf(s[qb][kb][r + 2], c, neg_m));
-                    const float p3 = exp2_fast(__builtin_fmaf(s[qb][kb][r + 3], c, neg_m));
-                    a0 += p0 + p1;
-                    a1 += p2 + p3;
-                    const int j = r >> 3, w = (r & 7) >> 1;
-                    pk[qb][kb][j][w] = pack2<T>(p0, p1);
-                    pk[qb][kb][j][w + 1] = pack2<T>(p2, p3);
-                }
-            rs[qb] = a0 + a1;
-        }
+        for (int e = 0; e < NP; ++e) pair_pack(pair_exp(s, m_run, c, e), e, pk, rs);
         // Materialise P here: otherwise the packing sinks below the rescale
         // branch and keeps every unpacked fp32 p alive across it.
 #pragma unroll
@@ -231,12 +305,86 @@ struct WaveTile {
             }
     }
 
-    // True when some lane's partial sum of this tile is out of range (or NaN-free inf).
-    static __device__ __forceinline__ bool needs_rescale(const float (&rs)[QB]) {
-        bool bad = false;
+    // Row maximum of the lane's query column over the tile (both wave halves).
+    static __device__ __forceinline__ float row_max(const f32x16 (&s)[QB][KB], int qb) {
+        float a = s[qb][0][0], b = s[qb][0][1];
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) bad |= !(rs[qb] <= kSumLimit);
-        return __builtin_amdgcn_ballot_w64(bad) != 0;
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int r = (kb == 0 ? 2 : 0); r < 16; r += 4) {
+                a = fmaxf(fmaxf(a, s[qb][kb][r]), s[qb][kb][r + 1]);
+                b = fmaxf(fmaxf(b, s[qb][kb][r + 2]), s[qb][kb][r + 3]);
+            }
+        return halves_max(fmaxf(a, b));
+    }
+
+    // A row's first tile: m = c * rowmax, so every p <= 1 and the sum cannot
+    // overflow.
+    static __device__ __forceinline__ void first(const f32x16 (&s)[QB][KB], float (&m_run)[QB], float (&l_run)[QB],
+                                                 float c, u32x4 (&pk)[QB][KB][2]) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) m_run[qb] = fmaxf(m_run[qb], row_max(s, qb) * c);
+        expo(s, m_run, c, pk, l_run);
+    }
+
+    // One steady pipelined step: S^T of tile t+1 (K in kn), O^T += V^T P^T of
+    // tile t-1 (V in vp, P in p_prv) and the softmax of tile t (s_cur -> p_cur).
+    // Written in issue order -- operand reads from LDS first, two pairs of
+    // scores exponentiated while they are in flight, then every MFMA followed by
+    // its share of the softmax -- and left to the compiler's scheduler (pinning
+    // the order measured slower).  Same arithmetic as qk + pv + expo.
+    static __device__ __forceinline__ void step(const FA_LDS char* kn, const FA_LDS char* vp, const int (&offk)[KS],
+                                                const int (&offv)[DB], const u32x4 (&qf)[QB][KS],
+                                                const f32x16 (&s_cur)[QB][KB], f32x16 (&s_nxt)[QB][KB],
+                                                const u32x4 (&p_prv)[QB][KB][2], u32x4 (&p_cur)[QB][KB][2],
+                                                f32x16 (&oacc)[QB][DB], const float (&m_run)[QB], float c,
+                                                float (&rs)[QB]) {
+        constexpr int NM = NQK + NPV;
+        constexpr int LEAD = 2;
+        u32x4 kf[KB][KS];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) kf[kb][ks] = k_frag(kn, offk, kb, ks);
+        u32x4 vf[KB][2][DB];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int db = 0; db < DB; ++db) vf[kb][j][db] = v_frag(vp, offv, kb, j, db);
+        Pair x[NP];
+        int nf = 0, nc = 0;
+#pragma unroll
+        for (; nf < LEAD; ++nf) x[nf] = pair_exp(s_cur, m_run, c, nf);
+        const f32x16 zero = {};
+#pragma unroll
+        for (int i = 0; i < NM; ++i) {
+            if (i < NQK) {
+                const int kb = i / (KS * QB), ks = (i / QB) % KS, qb = i % QB;
+                s_nxt[qb][kb] = mfma32x32x16<T>(kf[kb][ks], qf[qb][ks], ks == 0 ? zero : s_nxt[qb][kb]);
+            } else {
+                const int u = i - NQK;
+                const int kb = u / (2 * DB * QB), j = (u / (DB * QB)) % 2, db = (u / QB) % DB, qb = u % QB;
+                oacc[qb][db] = mfma32x32x16<T>(vf[kb][j][db], p_prv[qb][kb][j], oacc[qb][db]);
+            }
+            // this slot's share: exponentials up to f_end, packing up to c_end
+            const int nf0 = nf;
+            const int f_end = i == NM - 1 ? NP : LEAD + ((i + 1) * (NP - LEAD) + NM / 2) / NM;
+            const int c_end = i == NM - 1 ? NP : min(((i + 1) * NP + NM / 2) / NM, nf0);
+#pragma unroll
+            for (; nf < f_end; ++nf) x[nf] = pair_exp(s_cur, m_run, c, nf);
+#pragma unroll
+            for (; nc < c_end; ++nc) pair_pack(x[nc], nc, p_cur, rs);
+        }
+    }
+
+    // True when some lane's partial sum of this tile is out of range (or inf).
+    static __device__ __forceinline__ bool needs_rescale(const float (&rs)[QB]) {
+        float mx = rs[0];
+#pragma unroll
+        for (int qb = 1; qb < QB; ++qb) mx = fmaxf(mx, rs[qb]);
+        return __builtin_amdgcn_ballot_w64(!(mx <= kSumLimit)) != 0;
     }
 
     // The exact path: move m to max(m, c * rowmax(S)), rescale l and acc by
@@ -246,15 +394,7 @@ struct WaveTile {
                                                    float (&rs)[QB]) {
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
-            float a = s[qb][0][0], b = s[qb][0][1];
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                for (int r = (kb == 0 ? 2 : 0); r < 16; r += 4) {
-                    a = fmaxf(fmaxf(a, s[qb][kb][r]), s[qb][kb][r + 1]);
-                    b = fmaxf(fmaxf(b, s[qb][kb][r + 2]), s[qb][kb][r + 3]);
-                }
-            const float m_new = fmaxf(m_run[qb], halves_max(fmaxf(a, b)) * c);
+            const float m_new = fmaxf(m_run[qb], row_max(s, qb) * c);
             const float alpha = exp2_fast(m_run[qb] - m_new);
             m_run[qb] = m_new;
             l_run[qb] *= alpha;
@@ -276,6 +416,7 @@ void fa_fwd_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
     constexpr int D = Cfg::D, QB = Cfg::QB, KB = Cfg::KB, KS = Cfg::KS, DB = Cfg::DB;
     constexpr int BN = Cfg::BN, BM = Cfg::BM, BMW = Cfg::BMW, RB = Cfg::RB;
     constexpr bool CAUSAL = Cfg::CAUSAL;
+    static_assert(!Cfg::PIPE || Cfg::TBN == BN, "the pipelined loop stages one compute tile per LDS tile");
 
     __shared__ __attribute__((aligned(1024))) char k_lds0[Cfg::TILE];
     __shared__ __attribute__((aligned(1024))) char k_lds1[Cfg::TILE];
@@ -286,7 +427,7 @@ void fa_fwd_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 31;  // MFMA output column = this lane's query within a 32-block
     const int h = lane >> 5;  // wave half
 
@@ -302,8 +443,10 @@ void fa_fwd_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
 
     const int64_t head = (int64_t)bh * S * D;
     const uint16_t* qh = Q + head;
-    const uint16_t* kh = K + head;
-    const uint16_t* vh = V + head;
+    const __amdgpu_buffer_rsrc_t krs = head_rsrc<T>(K + head, S * RB);
+    const __amdgpu_buffer_rsrc_t vrs = head_rsrc<T>(V + head, S * RB);
+    const uint32_t koff = tile_lane_offset<Cfg, false>(wave, lane);
+    const uint32_t voff = tile_lane_offset<Cfg, true>(wave, lane);
 
     const int kend = CAUSAL ? min(q0 + BM, S) : S;
     const int ntiles = (kend + BN - 1) / BN;
@@ -313,11 +456,11 @@ void fa_fwd_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
 
     // First tiles in flight before anything else: K(0) and, pipelined, K(1);
     // otherwise K(0) and V(0).
-    load_tile<Cfg, false>(kbuf[0], kh, 0, S, wave, lane);
+    load_tile<T, Cfg, false>(kbuf[0], krs, koff, 0, wave, lane);
     if constexpr (Cfg::PIPE) {
-        if (ntiles > 1) load_tile<Cfg, false>(kbuf[1], kh, BN, S, wave, lane);
+        if (ntiles > 1) load_tile<T, Cfg, false>(kbuf[1], krs, koff, BN, wave, lane);
     } else {
-        load_tile<Cfg, true>(vbuf[0], vh, 0, S, wave, lane);
+        load_tile<T, Cfg, true>(vbuf[0], vrs, voff, 0, wave, lane);
     }
 
     // Q^T operand fragments: lane holds Q[query][16ks + 8h .. +7].  Rows beyond
@@ -371,52 +514,6 @@ void fa_fwd_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
     f32x16 sA[QB][KB], sB[QB][KB];
     u32x4 pA[QB][KB][2], pB[QB][KB][2];
 
-    if constexpr (Cfg::PIPE) {
-        wait_vmcnt0();
-        __syncthreads();
-        if (wtiles > 0) W::qk(kbuf[0], offk, qf, sA);
-    }
-
-    // Iteration t: S(t) in s_cur, S(t+1) goes to s_nxt, P(t-1) in p_prv, P(t)
-    // goes to p_cur; K(t) / V(t) live in buffer t&1, K(t+1) / V(t-1) in the other.
-    // STEADY iterations (1 <= t, t+1 < wtiles, tile t unmasked) are branch-free
-    // so that their MFMAs and exponentials form one basic block.
-    auto iter = [&](auto steady, int t, FA_LDS char* kc, FA_LDS char* kn, FA_LDS char* vc, FA_LDS char* vp,
-                    f32x16 (&s_cur)[QB][KB], f32x16 (&s_nxt)[QB][KB], u32x4 (&p_prv)[QB][KB][2],
-                    u32x4 (&p_cur)[QB][KB][2]) {
-        constexpr bool STEADY = decltype(steady)::value;
-        const int k0 = t * BN;
-        wait_vmcnt0();
-        __syncthreads();  // K(t+1) and V(t-1) visible; K(t) and V(t-2) no longer read
-        // (a transfer past the last tile only re-reads clamped rows into a free buffer)
-        if (STEADY || t + 2 < ntiles) load_tile<Cfg, false>(kc, kh, k0 + 2 * BN, S, wave, lane);
-        load_tile<Cfg, true>(vc, vh, k0, S, wave, lane);
-
-        float rs[QB];
-        if constexpr (STEADY) {
-            W::qk(kn, offk, qf, s_nxt);
-            W::pv(vp, offv, p_prv, oacc);
-            W::expo(s_cur, m_run, c, p_cur, rs);
-        } else {
-            const bool do_qk = t + 1 < wtiles;
-            const bool do_pv = t >= 1 && t <= wtiles;
-            if (t >= wtiles) {
-                if (do_pv) W::pv(vp, offv, p_prv, oacc);  // this wave's last tile, while V(t-1) is resident
-                return;
-            }
-            if (do_qk) W::qk(kn, offk, qf, s_nxt);
-            if (do_pv) W::pv(vp, offv, p_prv, oacc);
-            if ((CAUSAL && k0 + BN - 1 > qw) || k0 + BN > S) W::mask(s_cur, last, k0, h);
-            W::expo(s_cur, m_run, c, p_cur, rs);
-        }
-        // P*V of tile t-1 is in acc now, so a rescale covers every earlier term.
-        if (W::needs_rescale(rs)) W::rescale(s_cur, m_run, l_run, oacc, c, p_cur, rs);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) l_run[qb] += rs[qb];
-    };
-    using Steady = std::true_type;
-    using Edge = std::false_type;
-
     if constexpr (!Cfg::PIPE) {
         // One LDS tile (TBN keys) per barrier; inside it, compute steps of BN
         // keys: S, (mask), softmax, P*V -- single register sets.
@@ -427,8 +524,8 @@ void fa_fwd_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
             wait_vmcnt0();
             __syncthreads();
             if (lt + 1 < nlds) {
-                load_tile<Cfg, false>(kn, kh, (lt + 1) * Cfg::TBN, S, wave, lane);
-                load_tile<Cfg, true>(vn, vh, (lt + 1) * Cfg::TBN, S, wave, lane);
+                load_tile<T, Cfg, false>(kn, krs, koff, (lt + 1) * Cfg::TBN, wave, lane);
+                load_tile<T, Cfg, true>(vn, vrs, voff, (lt + 1) * Cfg::TBN, wave, lane);
             }
 #pragma unroll
             for (int sub = 0; sub < SUB; ++sub) {
@@ -437,11 +534,15 @@ void fa_fwd_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
                 const int k0 = t * BN;
                 W::qk(kc + sub * BN * RB, offk, qf, sA);
                 if ((CAUSAL && k0 + BN - 1 > qw) || k0 + BN > S) W::mask(sA, last, k0, h);
-                float rs[QB];
-                W::expo(sA, m_run, c, pA, rs);
-                if (W::needs_rescale(rs)) W::rescale(sA, m_run, l_run, oacc, c, pA, rs);
+                if (t == 0) {
+                    W::first(sA, m_run, l_run, c, pA);
+                } else {
+                    float rs[QB];
+                    W::expo(sA, m_run, c, pA, rs);
+                    if (W::needs_rescale(rs)) W::rescale(sA, m_run, l_run, oacc, c, pA, rs);
 #pragma unroll
-                for (int qb = 0; qb < QB; ++qb) l_run[qb] += rs[qb];
+                    for (int qb = 0; qb < QB; ++qb) l_run[qb] += rs[qb];
+                }
                 W::pv(vc + sub * BN * RB, offv, pA, oacc);
             }
         };
@@ -450,27 +551,76 @@ void fa_fwd_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
             if (lt + 1 < nlds) simple(lt + 1, kbuf[1], vbuf[1], kbuf[0], vbuf[0]);
         }
     } else {
-    // leading tiles that need no mask for any of this wave's rows
-    const int unmasked = min(CAUSAL ? (qw + 1) / BN : ntiles, S / BN);
-    const int steady_end = min(wtiles - 1, unmasked);  // steady for 1 <= t < steady_end
+        wait_vmcnt0();
+        __syncthreads();
+        if (wtiles > 0) W::qk(kbuf[0], offk, qf, sA);
 
-    iter(Edge{}, 0, kbuf[0], kbuf[1], vbuf[0], vbuf[1], sA, sB, pA, pB);
-    int t = 1;
-    for (; t + 1 < steady_end; t += 2) {
-        iter(Steady{}, t, kbuf[1], kbuf[0], vbuf[1], vbuf[0], sB, sA, pB, pA);
-        iter(Steady{}, t + 1, kbuf[0], kbuf[1], vbuf[0], vbuf[1], sA, sB, pA, pB);
-    }
-    for (; t < ntiles; t += 2) {
-        iter(Edge{}, t, kbuf[1], kbuf[0], vbuf[1], vbuf[0], sB, sA, pB, pA);
-        if (t + 1 < ntiles) iter(Edge{}, t + 1, kbuf[0], kbuf[1], vbuf[0], vbuf[1], sA, sB, pA, pB);
-    }
-    // drain: P*V of the last tile for waves that attend to every tile
-    wait_vmcnt0();
-    __syncthreads();
-    if (wtiles == ntiles && wtiles > 0) {
-        if ((ntiles - 1) & 1) W::pv(vbuf[1], offv, pA, oacc);
-        else W::pv(vbuf[0], offv, pB, oacc);
-    }
+        // Iteration t: S(t) in s_cur, S(t+1) goes to s_nxt, P(t-1) in p_prv, P(t)
+        // goes to p_cur; K(t) / V(t) live in buffer t&1, K(t+1) / V(t-1) in the
+        // other.  Steady iterations (1 <= t, t+1 < wtiles, tile t unmasked) are
+        // branch-free so that their MFMAs and exponentials form one basic block.
+        auto iter = [&](auto kind, int t, FA_LDS char* kc, FA_LDS char* kn, FA_LDS char* vc, FA_LDS char* vp,
+                        f32x16 (&s_cur)[QB][KB], f32x16 (&s_nxt)[QB][KB], u32x4 (&p_prv)[QB][KB][2],
+                        u32x4 (&p_cur)[QB][KB][2]) __attribute__((always_inline)) {
+            constexpr int KIND = decltype(kind)::value;  // 0 first, 1 steady, 2 edge
+            const int k0 = t * BN;
+            wait_vmcnt0();
+            __syncthreads();  // K(t+1) and V(t-1) visible; K(t) and V(t-2) no longer read
+            if (KIND == 1 || t + 2 < ntiles) load_tile<T, Cfg, false>(kc, krs, koff, k0 + 2 * BN, wave, lane);
+            load_tile<T, Cfg, true>(vc, vrs, voff, k0, wave, lane);
+
+            if constexpr (KIND == 0) {
+                if (t >= wtiles) return;
+                if (t + 1 < wtiles) W::qk(kn, offk, qf, s_nxt);
+                if ((CAUSAL && k0 + BN - 1 > qw) || k0 + BN > S) W::mask(s_cur, last, k0, h);
+                W::first(s_cur, m_run, l_run, c, p_cur);
+                return;
+            }
+            float rs[QB];
+            if constexpr (KIND == 1) {
+                W::step(kn, vp, offk, offv, qf, s_cur, s_nxt, p_prv, p_cur, oacc, m_run, c, rs);
+            } else {
+                const bool do_qk = t + 1 < wtiles;
+                const bool do_pv = t <= wtiles;
+                if (t >= wtiles) {
+                    if (do_pv) W::pv(vp, offv, p_prv, oacc);  // this wave's last tile, while V(t-1) is resident
+                    return;
+                }
+                if (do_qk) W::qk(kn, offk, qf, s_nxt);
+                W::pv(vp, offv, p_prv, oacc);
+                if ((CAUSAL && k0 + BN - 1 > qw) || k0 + BN > S) W::mask(s_cur, last, k0, h);
+                W::expo(s_cur, m_run, c, p_cur, rs);
+            }
+            // P*V of tile t-1 is in acc now, so a rescale covers every earlier term.
+            if (W::needs_rescale(rs)) W::rescale(s_cur, m_run, l_run, oacc, c, p_cur, rs);
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) l_run[qb] += rs[qb];
+        };
+        using First = std::integral_constant<int, 0>;
+        using Steady = std::integral_constant<int, 1>;
+        using Edge = std::integral_constant<int, 2>;
+
+        // leading tiles that need no mask for any of this wave's rows
+        const int unmasked = min(CAUSAL ? (qw + 1) / BN : ntiles, S / BN);
+        const int steady_end = min(wtiles - 1, unmasked);  // steady for 1 <= t < steady_end
+
+        iter(First{}, 0, kbuf[0], kbuf[1], vbuf[0], vbuf[1], sA, sB, pA, pB);
+        int t = 1;
+        for (; t + 1 < steady_end; t += 2) {
+            iter(Steady{}, t, kbuf[1], kbuf[0], vbuf[1], vbuf[0], sB, sA, pB, pA);
+            iter(Steady{}, t + 1, kbuf[0], kbuf[1], vbuf[0], vbuf[1], sA, sB, pA, pB);
+        }
+        for (; t < ntiles; t += 2) {
+            iter(Edge{}, t, kbuf[1], kbuf[0], vbuf[1], vbuf[0], sB, sA, pB, pA);
+            if (t + 1 < ntiles) iter(Edge{}, t + 1, kbuf[0], kbuf[1], vbuf[0], vbuf[1], sA, sB, pA, pB);
+        }
+        // drain: P*V of the last tile for waves that attend to every tile
+        wait_vmcnt0();
+        __syncthreads();
+        if (wtiles == ntiles && wtiles > 0) {
+            if ((ntiles - 1) & 1) W::pv(vbuf[1], offv, pA, oacc);
+            else W::pv(vbuf[0], offv, pB, oacc);
+        }
     }
 
     // ---- epilogue: O = acc / l, lse = ln2 * (m + log2 l) ---------------------------

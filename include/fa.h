@@ -47,7 +47,8 @@ extern "C" {
 #define FA_ERR_CAUSAL 5         /* causal is not 0 or 1 */
 #define FA_ERR_SCALE 6          /* scale is not finite or not > 0 */
 #define FA_ERR_ALIAS 7          /* o or lse overlaps q, k, v or each other */
-#define FA_ERR_TOO_LARGE 8      /* sizes overflow the kernels' index ranges */
+#define FA_ERR_TOO_LARGE 8      /* sizes overflow the kernels' index ranges (for fp16 / bf16
+                                   also: one head's K or V, S * D * 2 bytes, must be < 2^31) */
 #define FA_ERR_LAUNCH 9         /* the HIP runtime rejected the kernel launch */
 #define FA_ERR_ALIGNMENT 10     /* q, k, v, o not 16-byte aligned, or lse not 4-byte aligned */
 

@@ -96,6 +96,7 @@ def call(fa, **over):
     (dict(B=1 << 31), "FA_ERR_TOO_LARGE"),
     (dict(S=1 << 31), "FA_ERR_TOO_LARGE"),
     (dict(B=1 << 20, H=1 << 20), "FA_ERR_TOO_LARGE"),
+    (dict(S=1 << 23, D=128), "FA_ERR_TOO_LARGE"),   # one head's K is 2 GiB: beyond a buffer extent
 ])
 def test_rejects_bad_arguments(fa, over, code):
     assert call(fa, **over) == _defines()[code]

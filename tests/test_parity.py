@@ -19,7 +19,9 @@ pytestmark = pytest.mark.gpu
 if not torch.cuda.is_available():
     pytest.skip("no GPU visible", allow_module_level=True)
 
-import exact_tiled_attention_06_amd as fa  # noqa: E402  (fails loudly when libfa.so is missing)
+import exact_tiled_attention_06_amd as fa  # noqa: E402
+
+fa.library()  # fails loudly when libfa.so is missing
 
 DEV = "cuda:0"
 
