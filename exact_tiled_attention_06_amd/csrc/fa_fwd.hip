@@ -14,6 +14,7 @@
 #include "../../include/fa.h"
 #include "fa_f32.hpp"
 #include "fa_mfma.hpp"
+#include "fa_ksplit.hpp"
 #include "fa_split.hpp"
 
 #ifndef FA_SPLIT_TBN
@@ -75,6 +76,20 @@ int launch_cfg(const void* q, const void* k, const void* v, void* o, float* lse,
     return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
+// Thin grids: workgroups of NW waves that share BMW query rows and split the keys.
+template <typename T, typename Cfg>
+int launch_ksplit(const void* q, const void* k, const void* v, void* o, float* lse, int S, int BH, float c,
+                  hipStream_t stream) {
+    const int n_qblk = (S + Cfg::BMW - 1) / Cfg::BMW;
+    const int64_t grid = (int64_t)n_qblk * BH;
+    if (grid > (int64_t)1 << 24) return FA_ERR_TOO_LARGE;
+    (void)hipGetLastError();
+    hipLaunchKernelGGL((fa_fwd_ksplit_kernel<T, Cfg>), dim3((unsigned)grid), dim3(Cfg::NT), 0, stream,
+                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, S, BH, n_qblk,
+                       c);
+    return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
 template <typename T, int D, bool CAUSAL>
 int launch_mfma(const void* q, const void* k, const void* v, void* o, float* lse, int S, int BH,
                 float c, hipStream_t stream) {
@@ -83,6 +98,11 @@ int launch_mfma(const void* q, const void* k, const void* v, void* o, float* lse
     using Small = MfmaConfig<D, CAUSAL, TL::SMALL_QB, TL::SMALL_NW, TL::SMALL_BN, TL::SMALL_PIPE>;
     const int64_t large_grid = (int64_t)((S + Large::BM - 1) / Large::BM) * BH;
     if (large_grid >= kFullGrid) return launch_cfg<T, Large>(q, k, v, o, lse, S, BH, c, stream);
+    if constexpr (D <= 64) {
+        // 64 query rows per workgroup, keys split over 4 waves
+        using KSplit = MfmaConfig<D, CAUSAL, 2, 4, 32>;
+        return launch_ksplit<T, KSplit>(q, k, v, o, lse, S, BH, c, stream);
+    }
     return launch_cfg<T, Small>(q, k, v, o, lse, S, BH, c, stream);
 }
 

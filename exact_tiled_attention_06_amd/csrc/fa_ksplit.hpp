@@ -1,0 +1,272 @@
+// fa_ksplit.hpp -- the matrix-core forward kernel for grids too small to fill
+// the GPU (few batch*head pairs): the waves of a workgroup share one block of
+// query rows and split its key range.
+//
+// A query block's rows are independent of every other block's, and so are
+// disjoint key ranges of one row, as long as the partial results are merged
+// with the log-sum-exp rule the saved lse exists for ("T5 讲解", section ⑥;
+// "Inside FlashAttention", section 2.4): over key ranges r with running
+// reference m_r, sum l_r and unnormalised output acc_r,
+//     M = max_r m_r,   l = sum_r 2^(m_r - M) l_r,   O = sum_r 2^(m_r - M) acc_r / l
+// (m in the exp2 domain of the kernel).  Wave w of the workgroup runs the same
+// Q-outer / K,V-inner online softmax as fa_mfma.hpp over the w-th contiguous
+// slice of the block's key tiles, streaming its own K/V tiles HBM -> LDS into
+// LDS buffers of its own, so the loop needs no barrier; at the end the waves
+// exchange (m, l, acc) through LDS and wave 0 merges and writes O and lse.
+// With NW waves per block, a thin grid gets NW times the waves and each row's
+// serial chain of tiles is NW times shorter, at the same HBM traffic (every
+// block still reads its key range once).
+#pragma once
+
+#include "fa_mfma.hpp"
+
+namespace fa {
+
+// Lane offsets for a wave that issues every transfer of a tile itself: the
+// swizzles repeat every 16 rows, i.e. every PER = RB / 64 transfers (at least 1),
+// so transfer i uses offset[i % PER] + (i / PER) * PER KiB.
+template <typename Cfg>
+struct WaveLoader {
+    static constexpr int PER = Cfg::RB >= 64 ? Cfg::RB / 64 : 1;
+    static constexpr int LOADS = Cfg::TILE / 1024;  // transfers per tile
+    static_assert(LOADS % PER == 0, "whole swizzle periods per tile");
+    template <bool ISV>
+    static __device__ __forceinline__ void offsets(int lane, uint32_t (&off)[PER]) {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) off[i] = tile_lane_offset<Cfg, ISV>(i, lane);
+    }
+    template <typename T>
+    static __device__ __forceinline__ void load(FA_LDS char* dst, __amdgpu_buffer_rsrc_t rsrc,
+                                                const uint32_t (&off)[PER], int k0) {
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i)
+            load_part<T, Cfg>(dst + i * 1024, rsrc, off[i % PER] + (uint32_t)((i / PER) * PER * 1024), k0);
+    }
+};
+
+template <typename T, typename Cfg>
+__global__ __attribute__((amdgpu_flat_work_group_size(Cfg::NT, Cfg::NT), amdgpu_waves_per_eu(Cfg::OCC, Cfg::OCC)))
+void fa_fwd_ksplit_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                          const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
+                          int S, int BH, int n_qblk, float c) {
+    using W = WaveTile<T, Cfg>;
+    using L = WaveLoader<Cfg>;
+    constexpr int D = Cfg::D, QB = Cfg::QB, KB = Cfg::KB, KS = Cfg::KS, DB = Cfg::DB;
+    constexpr int NW = Cfg::NW, BN = Cfg::BN, BMW = Cfg::BMW, RB = Cfg::RB, TILE = Cfg::TILE;
+    constexpr bool CAUSAL = Cfg::CAUSAL;
+    static_assert(Cfg::PIPE && Cfg::TBN == BN, "pipelined loop, one compute tile per LDS tile");
+
+    // Per wave: two K and two V tiles.  After the loop the same memory holds
+    // the exchange of waves 1..NW-1: per lane QB*DB*16 accumulators, QB m, QB l.
+    constexpr int XCH = (QB * DB * 16 + 2 * QB) * 64 * 4;  // bytes per wave
+    constexpr int LDS_BYTES = NW * 4 * TILE > (NW - 1) * XCH ? NW * 4 * TILE : (NW - 1) * XCH;
+    __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n = lane & 31;
+    const int h = lane >> 5;
+    FA_LDS char* const mine = (FA_LDS char*)lds + wave * 4 * TILE;
+    FA_LDS char* const kbuf[2] = {mine, mine + TILE};
+    FA_LDS char* const vbuf[2] = {mine + 2 * TILE, mine + 3 * TILE};
+
+    // Workgroup -> (head, query block): heads vary fastest, causal blocks
+    // longest first.  Every wave holds the block's BMW rows.
+    const int wg = blockIdx.x;
+    const int bh = wg % BH;
+    const int rank = wg / BH;
+    const int qblk = CAUSAL ? (n_qblk - 1 - rank) : rank;
+    const int q0 = qblk * BMW;
+
+    const int64_t head = (int64_t)bh * S * D;
+    const uint16_t* qh = Q + head;
+    const __amdgpu_buffer_rsrc_t krs = head_rsrc<T>(K + head, S * RB);
+    const __amdgpu_buffer_rsrc_t vrs = head_rsrc<T>(V + head, S * RB);
+    uint32_t koff[L::PER], voff[L::PER];
+    L::template offsets<false>(lane, koff);
+    L::template offsets<true>(lane, voff);
+
+    // This wave's slice [tb, te) of the block's key tiles.
+    const int kend = CAUSAL ? min(q0 + BMW, S) : S;
+    const int ntiles = (kend + BN - 1) / BN;
+    const int tb = wave * ntiles / NW;
+    const int te = (wave + 1) * ntiles / NW;
+    const int nt = te - tb;
+
+    u32x4 qf[QB][KS];
+    int last[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        const int qrow = min(q0 + qb * 32 + n, S - 1);
+        last[qb] = CAUSAL ? qrow : S - 1;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            qf[qb][ks] = *reinterpret_cast<const u32x4*>(qh + (int64_t)qrow * D + ks * 16 + h * 8);
+            pin(qf[qb][ks]);
+        }
+    }
+
+    int offk[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) offk[ks] = n * RB + (((2 * ks + h) ^ swz_k<D>(n)) * 16);
+    const int r16 = lane & 15;
+    const int g16 = lane >> 4;
+    const int vrow = 4 * h + (r16 >> 2);
+    int offv[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+        const int dim = (32 * db + 16 * (g16 & 1) + 4 * (r16 & 3)) % D;
+        offv[db] = vrow * RB + (((dim >> 3) ^ swz_v<D>(vrow)) * 16) + (dim & 7) * 2;
+    }
+
+    float m_run[QB], l_run[QB];
+    f32x16 oacc[QB][DB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        m_run[qb] = kMInit;
+        l_run[qb] = 0.f;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[qb][db][r] = 0.f;
+    }
+
+    if (nt > 0) {
+        // Relative tile u = t - tb lives in buffers u & 1.  Iteration u: S(u) in
+        // s_cur, S(u+1) to s_nxt, P(u-1) in p_prv, P(u) to p_cur; K(u+2) and V(u)
+        // start into the buffers K(u) and V(u-2) left (their reads ended in
+        // iteration u-1: this wave is their only reader, so no barrier).
+        f32x16 sA[QB][KB], sB[QB][KB];
+        u32x4 pA[QB][KB][2], pB[QB][KB][2];
+        L::template load<T>(kbuf[0], krs, koff, tb * BN);
+        if (nt > 1) L::template load<T>(kbuf[1], krs, koff, (tb + 1) * BN);
+        wait_vmcnt0();
+        W::qk(kbuf[0], offk, qf, sA);
+
+        // rows whose tiles need no mask: tiles before the block's first row
+        // and before the end of the sequence
+        const int unmasked = min(CAUSAL ? (q0 + 1) / BN : ntiles, S / BN);
+        auto iter = [&](auto kind, int u, FA_LDS char* kc, FA_LDS char* kn, FA_LDS char* vc, FA_LDS char* vp,
+                        f32x16 (&s_cur)[QB][KB], f32x16 (&s_nxt)[QB][KB], u32x4 (&p_prv)[QB][KB][2],
+                        u32x4 (&p_cur)[QB][KB][2]) __attribute__((always_inline)) {
+            constexpr int KIND = decltype(kind)::value;  // 0 first, 1 steady, 2 edge
+            const int t = tb + u;
+            const int k0 = t * BN;
+            wait_vmcnt0();  // K(u+1) and V(u-1) landed
+            if (KIND == 1 || u + 2 < nt) L::template load<T>(kc, krs, koff, k0 + 2 * BN);
+            L::template load<T>(vc, vrs, voff, k0);
+            if constexpr (KIND == 0) {
+                if (u + 1 < nt) W::qk(kn, offk, qf, s_nxt);
+                if ((CAUSAL && k0 + BN - 1 > q0) || k0 + BN > S) W::mask(s_cur, last, k0, h);
+                W::first(s_cur, m_run, l_run, c, p_cur);
+                return;
+            }
+            float rs[QB];
+            if constexpr (KIND == 1) {
+                W::step(kn, vp, offk, offv, qf, s_cur, s_nxt, p_prv, p_cur, oacc, m_run, c, rs);
+            } else {
+                if (u + 1 < nt) W::qk(kn, offk, qf, s_nxt);
+                W::pv(vp, offv, p_prv, oacc);
+                if ((CAUSAL && k0 + BN - 1 > q0) || k0 + BN > S) W::mask(s_cur, last, k0, h);
+                W::expo(s_cur, m_run, c, p_cur, rs);
+            }
+            if (W::needs_rescale(rs)) W::rescale(s_cur, m_run, l_run, oacc, c, p_cur, rs);
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) l_run[qb] += rs[qb];
+        };
+        using First = std::integral_constant<int, 0>;
+        using Steady = std::integral_constant<int, 1>;
+        using Edge = std::integral_constant<int, 2>;
+        // steady for 1 <= u < u_steady: a next tile exists and this tile needs no mask
+        const int u_steady = min(nt - 1, unmasked - tb);
+        iter(First{}, 0, kbuf[0], kbuf[1], vbuf[0], vbuf[1], sA, sB, pA, pB);
+        int u = 1;
+        for (; u + 1 < u_steady; u += 2) {
+            iter(Steady{}, u, kbuf[1], kbuf[0], vbuf[1], vbuf[0], sB, sA, pB, pA);
+            iter(Steady{}, u + 1, kbuf[0], kbuf[1], vbuf[0], vbuf[1], sA, sB, pA, pB);
+        }
+        for (; u < nt; u += 2) {
+            iter(Edge{}, u, kbuf[1], kbuf[0], vbuf[1], vbuf[0], sB, sA, pB, pA);
+            if (u + 1 < nt) iter(Edge{}, u + 1, kbuf[0], kbuf[1], vbuf[0], vbuf[1], sA, sB, pA, pB);
+        }
+        // P*V of the last tile, whose V is in buffer (nt-1) & 1
+        wait_vmcnt0();
+        if ((nt - 1) & 1) W::pv(vbuf[1], offv, pA, oacc);
+        else W::pv(vbuf[0], offv, pB, oacc);
+    }
+
+    // ---- merge the waves' partial results, then the epilogue ------------------------
+    __syncthreads();  // every wave is done with its K/V buffers
+    float* const xch = (float*)lds;
+    auto slot = [&](int w, int k) __attribute__((always_inline)) -> float& {
+        return xch[((w - 1) * (QB * DB * 16 + 2 * QB) + k) * 64 + lane];
+    };
+    if (wave > 0) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) slot(wave, (qb * DB + db) * 16 + r) = oacc[qb][db][r];
+            slot(wave, QB * DB * 16 + qb) = m_run[qb];
+            slot(wave, QB * DB * 16 + QB + qb) = l_run[qb];
+        }
+    }
+    __syncthreads();
+    if (wave != 0) return;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        float mw[NW];
+        mw[0] = m_run[qb];
+        float mx = mw[0];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) {
+            mw[w] = slot(w, QB * DB * 16 + qb);
+            mx = fmaxf(mx, mw[w]);
+        }
+        const float a0 = exp2_fast(mw[0] - mx);
+        float l = l_run[qb] * a0;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[qb][db][r] *= a0;
+#pragma unroll
+        for (int w = 1; w < NW; ++w) {
+            const float aw = exp2_fast(mw[w] - mx);
+            l += aw * slot(w, QB * DB * 16 + QB + qb);
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[qb][db][r] += aw * slot(w, (qb * DB + db) * 16 + r);
+        }
+        m_run[qb] = mx;
+        l_run[qb] = l;
+    }
+
+    uint16_t* oh = O + head;
+    float* lh = LSE + (int64_t)bh * S;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        const float l = halves_sum(l_run[qb]);
+        const float inv = 1.0f / l;
+        const int qrow = q0 + qb * 32 + n;
+        if (qrow < S) {
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int d = db * 32 + 8 * g + 4 * h;
+                    if (d < D) {
+                        u32x2 w;
+                        w[0] = pack2<T>(oacc[qb][db][4 * g + 0] * inv, oacc[qb][db][4 * g + 1] * inv);
+                        w[1] = pack2<T>(oacc[qb][db][4 * g + 2] * inv, oacc[qb][db][4 * g + 3] * inv);
+                        *reinterpret_cast<u32x2*>(oh + (int64_t)qrow * D + d) = w;
+                    }
+                }
+            if (h == 0) lh[qrow] = kLn2 * (m_run[qb] + log2_fast(l));
+        }
+    }
+}
+
+}  // namespace fa
