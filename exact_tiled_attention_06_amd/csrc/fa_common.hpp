@@ -22,6 +22,9 @@ struct BF16 {};
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_inff();
+// Initial running reference: finite and far below any score, so that the first
+// tile always takes the rescale path and exp2(m_init - m_new) is exactly 0.
+constexpr float kMInit = -1.0e30f;
 
 // D(32x32, fp32) += A(32x16) * B(16x32) on the matrix cores.  Per lane l of
 // the wave: A holds row l%32, k = 8*(l/32) .. +7; B holds column l%32,

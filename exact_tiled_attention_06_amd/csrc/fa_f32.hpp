@@ -1,12 +1,18 @@
 // fa_f32.hpp -- FlashAttention-2 forward for fp32 inputs (all arithmetic in fp32).
 //
-// The same Q-outer / K,V-inner online softmax as the matrix-core kernel, on the
-// vector ALUs: one thread owns one query row (its q, its fp32 accumulator and
-// its running m, l stay in registers), a workgroup of 64 threads owns 64
-// consecutive rows, and each key/value tile of 32 rows is staged once in LDS
-// and read by all 64 threads as broadcasts.  The softmax weights stay fp32
-// for the P*V product: there is no lower-precision matrix input to round to.
-// Causal workgroups stop at their last row's diagonal and mask only the tiles
+// The same Q-outer / K,V-inner online softmax as the matrix-core kernels, on the
+// vector ALUs: a workgroup owns 64 query rows, one per lane, and its NW waves
+// split the block's keys into contiguous slices.  Every lane of a wave needs the
+// same key and value row at the same time, so K and V are read with wave-uniform
+// addresses (scalar loads through the scalar cache) and enter the FMAs as
+// scalar operands; each dot product runs as 8 independent partial sums.  Keys
+// are taken BN at a time: scores, their maximum, one rescale of the running
+// state, then the weighted sum of value rows ("从零训练语言模型（第二部分）",
+// section "安全 / 在线 softmax").  The softmax weights stay fp32 for the P*V
+// product: there is no lower-precision matrix input to round to.  The waves'
+// partial results are merged with the log-sum-exp rule through LDS (the merge
+// the saved lse enables: "T5 讲解", section ⑥), and wave 0 writes O and lse.
+// Causal workgroups stop at their last row's diagonal and mask only the keys
 // that cross it ("Triton 实现", section "Causal Mask 的处理"; "T5 讲解",
 // section ⑤).
 #pragma once
@@ -15,80 +21,111 @@
 
 namespace fa {
 
-constexpr int F32_BM = 64;  // query rows per workgroup (one wave)
-constexpr int F32_BN = 32;  // keys per LDS tile
+constexpr int F32_BM = 64;  // query rows per workgroup (one per lane)
+// The running reference m moves only when a key's scaled score exceeds it by
+// more than this (log2 units), so weights stay below 2^8 and the exact
+// rescale runs a few times per row instead of at every key.
+constexpr float kF32Margin = 8.0f;
+
+// Waves per workgroup (key slices); the merge buffer, (NW-1) * (D+2) floats
+// per lane, must fit in LDS.
+template <int D>
+struct F32Cfg {
+    static constexpr int NW = D == 128 ? 4 : 8;
+    static constexpr int NT = 64 * NW;
+};
 
 template <int D, bool CAUSAL>
-__global__ __attribute__((amdgpu_flat_work_group_size(F32_BM, F32_BM)))
+__global__ __attribute__((amdgpu_flat_work_group_size(F32Cfg<D>::NT, F32Cfg<D>::NT)))
 void fa_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                        const float* __restrict__ V, float* __restrict__ O, float* __restrict__ LSE,
                        int S, int BH, int n_qblk, float c) {
-    __shared__ float ks[F32_BN][D];
-    __shared__ float vs[F32_BN][D];
+    constexpr int NW = F32Cfg<D>::NW;
+    constexpr int XW = D + 2;  // floats per lane in the merge: acc, m, l
+    __shared__ float xch[(NW - 1) * XW * 64];
 
     const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wg = blockIdx.x;
     const int bh = wg % BH;
     const int rank = wg / BH;
     const int qblk = CAUSAL ? (n_qblk - 1 - rank) : rank;
     const int q0 = qblk * F32_BM;
-    const int qrow = q0 + tid;
+    const int qrow = q0 + lane;
     const int64_t head = (int64_t)bh * S * D;
+    const float* kh = K + head;
+    const float* vh = V + head;
 
     float q[D], acc[D];
+    const int qsrc = min(qrow, S - 1);
 #pragma unroll
     for (int d = 0; d < D; ++d) {
-        q[d] = (qrow < S) ? Q[head + (int64_t)qrow * D + d] : 0.f;
+        q[d] = Q[head + (int64_t)qsrc * D + d];
         acc[d] = 0.f;
     }
-    float m_run = kNegInf, l_run = 0.f;
+    float m_run = kMInit, l_run = 0.f;
 
+    // this wave's slice [kb, ke) of the block's keys
     const int kend = CAUSAL ? min(q0 + F32_BM, S) : S;
-    for (int k0 = 0; k0 < kend; k0 += F32_BN) {
-        // stage K and V rows k0 .. k0+31 (zero beyond S); coalesced over d
-        for (int e = tid; e < F32_BN * D; e += F32_BM) {
-            const int r = e / D, d = e % D;
-            const bool ok = k0 + r < S;
-            ks[r][d] = ok ? K[head + (int64_t)(k0 + r) * D + d] : 0.f;
-            vs[r][d] = ok ? V[head + (int64_t)(k0 + r) * D + d] : 0.f;
+    const int kb = wave * kend / NW;
+    const int ke = (wave + 1) * kend / NW;
+    for (int key = kb; key < ke; ++key) {
+        const float* kr = kh + (int64_t)key * D;
+        float part[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) part[i] = 0.f;
+#pragma unroll
+        for (int d = 0; d < D; ++d) part[d & 7] = __builtin_fmaf(q[d], kr[d], part[d & 7]);
+        float sc = (((part[0] + part[1]) + (part[2] + part[3])) + ((part[4] + part[5]) + (part[6] + part[7]))) * c;
+        if (CAUSAL && key > qrow) sc = kNegInf;
+        // move the reference only when a weight would exceed 2^kF32Margin
+        if (__builtin_amdgcn_ballot_w64(sc > m_run + kF32Margin)) {
+            const float m_new = fmaxf(m_run, sc);
+            const float alpha = exp2_fast(m_run - m_new);
+            m_run = m_new;
+            l_run *= alpha;
+#pragma unroll
+            for (int d = 0; d < D; ++d) acc[d] *= alpha;
         }
-        __syncthreads();
+        const float p = exp2_fast(sc - m_run);
+        l_run += p;
+        const float* vr = vh + (int64_t)key * D;
+#pragma unroll
+        for (int d = 0; d < D; ++d) acc[d] = __builtin_fmaf(p, vr[d], acc[d]);
+    }
 
-        float s[F32_BN];
-        float mx = kNegInf;
+    // ---- merge the waves' slices: M = max m, l = sum 2^(m-M) l, acc likewise ----
+    if (wave > 0) {
+        float* x = xch + (wave - 1) * XW * 64 + lane;
 #pragma unroll
-        for (int j = 0; j < F32_BN; ++j) {
-            float dot = 0.f;
+        for (int d = 0; d < D; ++d) x[d * 64] = acc[d];
+        x[D * 64] = m_run;
+        x[(D + 1) * 64] = l_run;
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    float mx = m_run;
 #pragma unroll
-            for (int d = 0; d < D; ++d) dot = __builtin_fmaf(q[d], ks[j][d], dot);
-            const int key = k0 + j;
-            const bool hidden = (key >= S) || (CAUSAL && key > qrow);
-            s[j] = hidden ? kNegInf : dot;
-            mx = fmaxf(mx, s[j]);
-        }
-        const float m_new = fmaxf(m_run, mx * c);
-        const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-        const float alpha = exp2_fast(m_run - m_use);
-        m_run = m_new;
-        float rs = 0.f;
+    for (int w = 1; w < NW; ++w) mx = fmaxf(mx, xch[((w - 1) * XW + D) * 64 + lane]);
+    const float a0 = exp2_fast(m_run - mx);
+    float l = l_run * a0;
 #pragma unroll
-        for (int d = 0; d < D; ++d) acc[d] *= alpha;
+    for (int d = 0; d < D; ++d) acc[d] *= a0;
 #pragma unroll
-        for (int j = 0; j < F32_BN; ++j) {
-            const float p = exp2_fast(__builtin_fmaf(s[j], c, -m_use));
-            rs += p;
+    for (int w = 1; w < NW; ++w) {
+        const float* x = xch + (w - 1) * XW * 64 + lane;
+        const float aw = exp2_fast(x[D * 64] - mx);
+        l += aw * x[(D + 1) * 64];
 #pragma unroll
-            for (int d = 0; d < D; ++d) acc[d] = __builtin_fmaf(p, vs[j][d], acc[d]);
-        }
-        l_run = l_run * alpha + rs;
-        __syncthreads();
+        for (int d = 0; d < D; ++d) acc[d] = __builtin_fmaf(aw, x[d * 64], acc[d]);
     }
 
     if (qrow < S) {
-        const float inv = 1.0f / l_run;
+        const float inv = 1.0f / l;
 #pragma unroll
         for (int d = 0; d < D; ++d) O[head + (int64_t)qrow * D + d] = acc[d] * inv;
-        LSE[(int64_t)bh * S + qrow] = kLn2 * (m_run + log2_fast(l_run));
+        LSE[(int64_t)bh * S + qrow] = kLn2 * (mx + log2_fast(l));
     }
 }
 

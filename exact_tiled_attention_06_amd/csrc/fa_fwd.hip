@@ -113,7 +113,7 @@ int launch_f32(const void* q, const void* k, const void* v, void* o, float* lse,
     const int64_t grid = (int64_t)n_qblk * BH;
     if (grid > (int64_t)1 << 24) return FA_ERR_TOO_LARGE;
     (void)hipGetLastError();
-    hipLaunchKernelGGL((fa_fwd_f32_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(F32_BM), 0, stream,
+    hipLaunchKernelGGL((fa_fwd_f32_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(F32Cfg<D>::NT), 0, stream,
                        (const float*)q, (const float*)k, (const float*)v, (float*)o, lse, S, BH, n_qblk,
                        c);
     return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;

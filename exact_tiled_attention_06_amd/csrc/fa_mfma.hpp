@@ -96,9 +96,6 @@ struct MfmaConfig {
 
 // A tile's partial row sums above this trigger the exact rescale path.
 constexpr float kSumLimit = 16384.0f;
-// Initial running reference: finite and far below any score, so that the first
-// tile always takes the rescale path and exp2(m_init - m_new) is exactly 0.
-constexpr float kMInit = -1.0e30f;
 
 // XOR swizzle of the 16-byte chunk index within a K row: one chunk read by 16
 // consecutive rows lands in 16 distinct (row parity, chunk) bank groups.

@@ -70,7 +70,7 @@ def test_small_shapes_elementwise(dtype, D, causal):
         full_check(q, k, v, causal, dtype, what=f"{dtype} D={D} causal={causal} B,H,S={B},{H},{S}")
 
 
-@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "f32"])
 @pytest.mark.parametrize("causal", [False, True])
 def test_growing_scores_force_rescales(dtype, causal):
     """Keys scaled up along the sequence make the running maximum grow on every tile,
@@ -84,7 +84,7 @@ def test_growing_scores_force_rescales(dtype, causal):
     full_check(q, k, v, causal, dtype, what="growing scores")
 
 
-@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "f32"])
 def test_scale_values(dtype):
     B, H, S, D = 1, 2, 300, 64
     q, k, v = workloads.make_inputs(B, H, S, D, dtype, 88)
