@@ -1,7 +1,8 @@
 """Double-precision CPU attention oracle (test infrastructure only).
 
-This package is the parity oracle: plain exact attention evaluated row by row in
-IEEE double precision (``attn_oracle.c``), with no tiling and no online softmax.
+This package is the parity oracle: plain exact attention and its gradients
+evaluated row by row in IEEE double precision (``attn_oracle.c``), with no
+tiling and no online softmax.
 Only the tests, the smoke check and the benchmark's CPU-baseline leg may import
 it.  It shares no code with the HIP path and imports nothing from the product
 package.
@@ -13,6 +14,10 @@ section 1.1), the stable softmax with the row maximum subtracted
 log-sum-exp ``lse = m + ln l`` ("Inside FlashAttention", section 2.4).  Causal
 means query ``i`` sees keys ``0..i`` ("Triton 实现", the naive listing's
 upper-triangular mask).
+
+The gradients (``attention_bwd``) follow the backward equations of
+"从零训练语言模型（第二部分）", section "反向传播", with the softmax Jacobian's row
+term taken as sum_t P_it dP_it from the oracle's own probabilities.
 
 Inputs are the *stored* element values the GPU receives (fp16, bf16 or fp32),
 widened exactly to float64 by the caller; ``scale`` is the float32 value that is
@@ -59,6 +64,12 @@ class Oracle:
         lib.oracle_attn_fwd_rows.restype = ctypes.c_int
         lib.oracle_attn_fwd_rows.argtypes = [_c_double_p] * 3 + [ctypes.c_int64] * 4 + [
             ctypes.c_int, ctypes.c_double, _c_int64_p, ctypes.c_int64, _c_double_p, _c_double_p]
+        lib.oracle_attn_bwd.restype = ctypes.c_int
+        lib.oracle_attn_bwd.argtypes = [_c_double_p] * 7 + [ctypes.c_int64] * 4 + [
+            ctypes.c_int, ctypes.c_double]
+        lib.oracle_attn_bwd_rows.restype = ctypes.c_int
+        lib.oracle_attn_bwd_rows.argtypes = [_c_double_p] * 4 + [ctypes.c_int64] * 4 + [
+            ctypes.c_int, ctypes.c_double, _c_int64_p, ctypes.c_int64] + [_c_double_p] * 3
         lib.oracle_num_threads.restype = ctypes.c_int
         lib.oracle_num_threads.argtypes = []
         self._lib = lib
@@ -105,6 +116,41 @@ class Oracle:
             raise ValueError(f"oracle_attn_fwd_rows failed with status {rc}")
         return o, lse
 
+    def attention_bwd(self, q, k, v, dout, causal: bool, scale: float):
+        """Gradients of exact attention for upstream gradient ``dout``.
+
+        q, k, v, dout: [B,H,S,D]; returns (dq, dk, dv), each [B,H,S,D].
+        """
+        q, k, v, dout = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(dout)
+        if q.ndim != 4 or any(x.shape != q.shape for x in (k, v, dout)):
+            raise ValueError("q, k, v, dout must share one [B,H,S,D] shape")
+        B, H, S, D = q.shape
+        dq, dk, dv = np.empty_like(q), np.empty_like(q), np.empty_like(q)
+        rc = self._lib.oracle_attn_bwd(self._ptr(q), self._ptr(k), self._ptr(v), self._ptr(dout),
+                                       self._ptr(dq), self._ptr(dk), self._ptr(dv),
+                                       B, H, S, D, int(bool(causal)), float(scale))
+        if rc != 0:
+            raise ValueError(f"oracle_attn_bwd failed with status {rc}")
+        return dq, dk, dv
+
+    def attention_bwd_rows(self, q, k, v, dout, causal: bool, scale: float, rows):
+        """Gradients at selected flat positions ``(b*H + h)*S + t``: dQ of query t
+        and dK, dV of key t.  Returns (dq [n,D], dk [n,D], dv [n,D])."""
+        q, k, v, dout = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(dout)
+        if q.ndim != 4 or any(x.shape != q.shape for x in (k, v, dout)):
+            raise ValueError("q, k, v, dout must share one [B,H,S,D] shape")
+        B, H, S, D = q.shape
+        rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        n = rows.shape[0]
+        dq, dk, dv = (np.empty((n, D), dtype=np.float64) for _ in range(3))
+        rc = self._lib.oracle_attn_bwd_rows(
+            self._ptr(q), self._ptr(k), self._ptr(v), self._ptr(dout), B, H, S, D,
+            int(bool(causal)), float(scale), rows.ctypes.data_as(_c_int64_p), n,
+            self._ptr(dq), self._ptr(dk), self._ptr(dv))
+        if rc != 0:
+            raise ValueError(f"oracle_attn_bwd_rows failed with status {rc}")
+        return dq, dk, dv
+
 
 _DEFAULT: Optional[Oracle] = None
 
@@ -127,3 +173,11 @@ def attention(q, k, v, causal: bool, scale: float):
 
 def attention_rows(q, k, v, causal: bool, scale: float, rows):
     return default().attention_rows(q, k, v, causal, scale, rows)
+
+
+def attention_bwd(q, k, v, dout, causal: bool, scale: float):
+    return default().attention_bwd(q, k, v, dout, causal, scale)
+
+
+def attention_bwd_rows(q, k, v, dout, causal: bool, scale: float, rows):
+    return default().attention_bwd_rows(q, k, v, dout, causal, scale, rows)

@@ -288,6 +288,116 @@ def pin_one_hot(orc):
     _close(o[0, 0], np.broadcast_to(v[0, 0, 3], (S, D)), 1e-12, "one-hot O")
 
 
+
+# ------------------------------------------------------------------ backward pins
+# The gradients are pinned to the forward oracle (already pinned above) through
+# finite differences, to invariants of exact softmax attention that hold for any
+# input, and to torch's float64 autograd of an explicitly written forward.
+
+
+def _loss_fd(orc, q, k, v, dout, causal, scale, name, h=1e-5):
+    """Central differences of L = sum(dout * O) with respect to q, k or v."""
+    base = {"q": q, "k": k, "v": v}
+    x = base[name]
+    g = np.zeros_like(x)
+    for idx in np.ndindex(x.shape):
+        vals = []
+        for step in (h, -h):
+            xs = x.copy()
+            xs[idx] += step
+            args = dict(base)
+            args[name] = xs
+            o, _ = orc.attention(args["q"], args["k"], args["v"], causal, scale)
+            vals.append(float(np.sum(o * dout)))
+        g[idx] = (vals[0] - vals[1]) / (2 * h)
+    return g
+
+
+def pin_bwd_finite_differences(orc):
+    """dQ, dK, dV equal central differences of sum(dO * O) taken through the forward
+    oracle (truncation ~h^2, rounding ~1e-16/h: agreement to 1e-7)."""
+    for causal in (False, True):
+        B, H, S, D = 1, 2, 6, 3
+        q, k, v, dout = (_rand((B, H, S, D), 200 + t) for t in range(4))
+        scale = 0.7
+        dq, dk, dv = orc.attention_bwd(q, k, v, dout, causal, scale)
+        for name, got in (("q", dq), ("k", dk), ("v", dv)):
+            fd = _loss_fd(orc, q, k, v, dout, causal, scale, name)
+            _close(got, fd, 1e-7, f"d{name} vs finite differences (causal={causal})")
+
+
+def pin_bwd_key_shift(orc):
+    """Adding one vector to every key leaves every row's softmax unchanged, so the
+    key gradients of a head sum to zero (causal too: row i's visible keys all shift)."""
+    for causal in (False, True):
+        B, H, S, D = 2, 2, 17, 5
+        q, k, v, dout = (_rand((B, H, S, D), 210 + t) for t in range(4))
+        _, dk, _ = orc.attention_bwd(q, k, v, dout, causal, 0.6)
+        _close(dk.sum(axis=2), np.zeros((B, H, D)), 1e-12, f"sum_j dK_j (causal={causal})")
+
+
+def pin_bwd_dv_mass(orc):
+    """Each row of P sums to one, so sum_j dV_j = sum_i dO_i."""
+    for causal in (False, True):
+        B, H, S, D = 1, 3, 15, 4
+        q, k, v, dout = (_rand((B, H, S, D), 220 + t) for t in range(4))
+        _, _, dv = orc.attention_bwd(q, k, v, dout, causal, 0.8)
+        _close(dv.sum(axis=2), dout.sum(axis=2), 1e-12, f"sum_j dV_j (causal={causal})")
+
+
+def pin_bwd_euler(orc):
+    """Scores are bilinear in q and k, so sum_i <dQ_i, Q_i> = sum_j <dK_j, K_j>
+    (both equal sum_ij dS_ij s_ij); catches a gradient routed to the wrong operand."""
+    for causal in (False, True):
+        B, H, S, D = 2, 1, 13, 6
+        q, k, v, dout = (_rand((B, H, S, D), 230 + t) for t in range(4))
+        dq, dk, _ = orc.attention_bwd(q, k, v, dout, causal, 0.5)
+        lhs = np.sum(dq * q, axis=(2, 3))
+        rhs = np.sum(dk * k, axis=(2, 3))
+        _close(lhs, rhs, 1e-12, f"Euler identity (causal={causal})")
+
+
+def pin_bwd_single_key(orc):
+    """S = 1: P = 1, so dV = dO and dS = 0 (dQ = dK = 0)."""
+    for causal in (False, True):
+        q, k, v, dout = (_rand((2, 2, 1, 4), 240 + t) for t in range(4))
+        dq, dk, dv = orc.attention_bwd(q, k, v, dout, causal, 1.1)
+        _close(dv, dout, 1e-15, "S=1 dV")
+        _close(dq, np.zeros_like(dq), 1e-15, "S=1 dQ")
+        _close(dk, np.zeros_like(dk), 1e-15, "S=1 dK")
+
+
+def pin_bwd_torch_autograd(orc):
+    """Small shapes against torch float64 autograd of softmax(scale Q K^T + mask) V."""
+    seed = 250
+    for causal in (False, True):
+        for (B, H, S, D) in [(1, 1, 3, 2), (1, 2, 9, 4), (2, 1, 16, 8)]:
+            q, k, v, dout = (_rand((B, H, S, D), seed + t) for t in range(4))
+            seed += 4
+            scale = 1.0 / math.sqrt(D)
+            tq, tk, tv = (torch.from_numpy(x.copy()).requires_grad_(True) for x in (q, k, v))
+            s = torch.matmul(tq, tk.transpose(-1, -2)) * scale
+            if causal:
+                s = s.masked_fill(~torch.from_numpy(_mask(S, True)), float("-inf"))
+            o = torch.matmul(torch.softmax(s, dim=-1), tv)
+            o.backward(torch.from_numpy(dout))
+            dq, dk, dv = orc.attention_bwd(q, k, v, dout, causal, scale)
+            for name, got, ref in (("dq", dq, tq.grad), ("dk", dk, tk.grad), ("dv", dv, tv.grad)):
+                _close(got, ref.numpy(), 1e-12, f"{name} vs torch autograd {B,H,S,D} causal={causal}")
+
+
+def pin_bwd_rows_entry(orc):
+    """The sampled entry point returns dQ of query t and dK, dV of key t exactly as the full call."""
+    for causal in (False, True):
+        B, H, S, D = 2, 2, 19, 3
+        q, k, v, dout = (_rand((B, H, S, D), 270 + t) for t in range(4))
+        dq, dk, dv = orc.attention_bwd(q, k, v, dout, causal, 0.9)
+        rows = np.array([0, 7, 18, 19, 40, B * H * S - 1, 57], dtype=np.int64)
+        rq, rk, rv = orc.attention_bwd_rows(q, k, v, dout, causal, 0.9, rows)
+        _close(rq, dq.reshape(-1, D)[rows], 1e-13, "rows entry dQ")
+        _close(rk, dk.reshape(-1, D)[rows], 1e-13, "rows entry dK")
+        _close(rv, dv.reshape(-1, D)[rows], 1e-13, "rows entry dV")
+
 ALL_PINS = [
     pin_worked_example,
     pin_normalisation,
@@ -303,4 +413,11 @@ ALL_PINS = [
     pin_heads_independent,
     pin_rows_entry,
     pin_one_hot,
+    pin_bwd_finite_differences,
+    pin_bwd_key_shift,
+    pin_bwd_dv_mass,
+    pin_bwd_euler,
+    pin_bwd_single_key,
+    pin_bwd_torch_autograd,
+    pin_bwd_rows_entry,
 ]

@@ -31,6 +31,22 @@ MUTANTS = {
     "acc_init_one": ("acc[d] = 0.0;", "acc[d] = 1.0;"),
     "l_init_one": ("double l = 0.0;", "double l = 1.0;"),
     "q_row_offset": ("q + flat * D", "q + bh * S * D"),
+    # backward
+    "bwd_drops_row_term": ("const double ds = w[j] * (g[j] - row);", "const double ds = w[j] * g[j];"),
+    "bwd_ds_without_p": ("const double ds = w[j] * (g[j] - row);", "const double ds = g[j] - row;"),
+    "bwd_row_term_sign": ("const double ds = w[j] * (g[j] - row);", "const double ds = w[j] * (g[j] + row);"),
+    "bwd_dq_no_scale": ("dq_i[d] += scale * ds * kr[d];", "dq_i[d] += ds * kr[d];"),
+    "bwd_dq_uses_v": ("dq_i[d] += scale * ds * kr[d];", "dq_i[d] += scale * ds * v_bh[j * D + d];"),
+    "bwd_dk_uses_k": ("dk_j[d] += scale * ds * q_i[d];", "dk_j[d] += scale * ds * kr[d];"),
+    "bwd_dv_uses_ds": ("dv_j[d] += w[j] * do_i[d];", "dv_j[d] += ds * do_i[d];"),
+    "bwd_dv_wrong_index": ("dv_j[d] += w[j] * do_i[d];", "dv_j[d] += w[j] * do_i[0];"),
+    "bwd_dp_wrong_row": ("const double *vr = v_bh + j * D;", "const double *vr = v_bh;"),
+    "bwd_unnormalised_p": ("w[j] /= total;", "w[j] /= 1.0;"),
+    "bwd_causal_sees_all": ("const int64_t n_keys = causal ? i + 1 : S;\n        const double *q_i = q_bh + i * D;",
+                            "const int64_t n_keys = S;\n        const double *q_i = q_bh + i * D;"),
+    "bwd_rows_p_not_normalised": ("const double p = exp(scale * acc - top[x]) / sum[x];",
+                                  "const double p = exp(scale * acc - top[x]);"),
+    "bwd_rows_key_range": ("for (int64_t i = causal ? t : 0; i < S; ++i) {", "for (int64_t i = 0; i < S; ++i) {"),
 }
 
 
