@@ -1,4 +1,4 @@
-"""FlashAttention-2 forward for AMD Instinct MI355X (gfx950): Python binding of libfa.so.
+"""FlashAttention-2 forward and backward for AMD Instinct MI355X (gfx950): Python binding of libfa.so.
 
 Argument marshalling only: every step of the attention runs in the HIP kernels
 behind the C ABI declared in ``include/fa.h``.  PyTorch supplies device memory
@@ -9,12 +9,17 @@ import this package before the library exists.
 
     fa_fwd(q, k, v, o, lse, B, H, S, D, causal, scale, dtype, stream)
         the C entry point with raw device pointers (ints) and sizes;
+    fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, S, D, causal, scale, dtype, stream)
+        the C backward entry point;
     fa_status_string(status)
         the C status description;
     forward(q, k, v, causal=False, scale=None) -> (o, lse)
         convenience on torch tensors [B,H,S,D]: allocates o (input dtype) and
         lse (float32 [B,H,S]) and calls fa_fwd on the current stream.  The
         default scale is 1/sqrt(D) ("T5 讲解：FlashAttention forward", section ⑥).
+    backward(q, k, v, o, lse, dout, causal=False, scale=None) -> (dq, dk, dv)
+        gradients for the upstream gradient dout, from the forward's o and lse;
+        allocates the outputs and the D workspace and calls fa_bwd.
 """
 from __future__ import annotations
 
@@ -59,6 +64,9 @@ def _load() -> ctypes.CDLL:
     lib.fa_fwd.restype = ctypes.c_int
     lib.fa_fwd.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_void_p] + [ctypes.c_int64] * 4 + [
         ctypes.c_int, ctypes.c_float, ctypes.c_int, ctypes.c_void_p]
+    lib.fa_bwd.restype = ctypes.c_int
+    lib.fa_bwd.argtypes = [ctypes.c_void_p] * 10 + [ctypes.c_int64] * 4 + [
+        ctypes.c_int, ctypes.c_float, ctypes.c_int, ctypes.c_void_p]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_status_string.argtypes = [ctypes.c_int]
     return lib
@@ -78,13 +86,13 @@ def library() -> ctypes.CDLL:
 
 class FaError(RuntimeError):
     def __init__(self, status: int):
-        super().__init__(f"fa_fwd failed: {fa_status_string(status)} (status {status})")
+        super().__init__(f"attention call failed: {fa_status_string(status)} (status {status})")
         self.status = status
 
 
 class FaValueError(ValueError):
     def __init__(self, status: int):
-        super().__init__(f"fa_fwd rejected its arguments: {fa_status_string(status)} (status {status})")
+        super().__init__(f"attention call rejected its arguments: {fa_status_string(status)} (status {status})")
         self.status = status
 
 
@@ -96,6 +104,13 @@ def fa_fwd(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, S: int, D: 
            causal: int, scale: float, dtype: int, stream: int) -> int:
     """The C entry point: raw device addresses and sizes; returns the status code."""
     return int(library().fa_fwd(q, k, v, o, lse, B, H, S, D, int(causal), float(scale), int(dtype), stream))
+
+
+def fa_bwd(q: int, k: int, v: int, o: int, dout: int, lse: int, dq: int, dk: int, dv: int, delta: int,
+           B: int, H: int, S: int, D: int, causal: int, scale: float, dtype: int, stream: int) -> int:
+    """The C backward entry point: raw device addresses and sizes; returns the status code."""
+    return int(library().fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, S, D, int(causal),
+                                float(scale), int(dtype), stream))
 
 
 def check(status: int) -> None:
@@ -137,3 +152,34 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = Fa
                     B, H, S, D, int(bool(causal)), scale, DTYPE_CODES[q.dtype], stream)
     check(status)
     return out, lse
+
+
+def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
+             dout: torch.Tensor, causal: bool = False, scale: float | None = None):
+    """Attention backward on [B,H,S,D] device tensors (fp16 / bf16): returns (dq, dk, dv).
+
+    o and lse are the forward's outputs for the same q, k, v, causal and scale;
+    the D = rowsum(dout * o) workspace is allocated here."""
+    ts = (q, k, v, o, dout)
+    if q.dim() != 4 or any(t.shape != q.shape for t in ts):
+        raise ValueError(f"q, k, v, o, dout must share one [B,H,S,D] shape")
+    if any(t.dtype != q.dtype for t in ts) or q.dtype not in (torch.float16, torch.bfloat16):
+        raise ValueError("q, k, v, o, dout must share dtype float16 or bfloat16")
+    if not all(t.is_cuda for t in ts + (lse,)):
+        raise RuntimeError("all tensors must be device tensors")
+    if not all(t.is_contiguous() for t in ts + (lse,)):
+        raise ValueError("all tensors must be contiguous")
+    B, H, S, D = q.shape
+    if lse.shape != (B, H, S) or lse.dtype != torch.float32:
+        raise ValueError("lse must be a float32 tensor of shape [B,H,S]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    scale = float(torch.tensor(scale, dtype=torch.float32))
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    delta = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    status = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+                    dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), B, H, S, D,
+                    int(bool(causal)), scale, DTYPE_CODES[q.dtype], stream)
+    check(status)
+    return dq, dk, dv

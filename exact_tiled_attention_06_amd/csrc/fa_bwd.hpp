@@ -1,0 +1,437 @@
+// fa_bwd.hpp -- FlashAttention-2 backward for fp16 / bf16 inputs on the gfx950
+// matrix cores.
+//
+// Gradients of O = softmax(scale * Q K^T) V for an upstream gradient dO, with
+// the probabilities recomputed block by block from the saved natural-log lse
+// instead of stored ("从零训练语言模型（第二部分）", sections "使用 LSE 连接正向和
+// 反向传播" and "反向传播"):
+//     P   = exp(scale * Q K^T - lse)        (masked keys: 0)
+//     dV  = P^T dO          dP = dO V^T
+//     dS  = P o (dP - D),   D_i = rowsum(dO_i o O_i)
+//     dQ  = scale * dS K    dK = scale * dS^T Q
+// Two kernels, no atomics:
+//   fa_bwd_dq_kernel    query blocks outer, K/V tiles inner (the forward's
+//                       schedule): dQ stays in registers.  It also forms D for
+//                       its rows from O and dO and writes it to a workspace.
+//   fa_bwd_dkdv_kernel  key blocks outer, Q/dO tiles inner (the schedule the
+//                       page gives for dK and dV): dK and dV stay in registers.
+// S and dP are recomputed by both, so the pair runs 7 tile products instead of
+// the 5 of a single pass that scatters dQ with atomics; in exchange every
+// output is written once, deterministically, in its input type.
+//
+// Layout conventions are the forward's (fa_mfma.hpp): 32x32x16 MFMAs; a wave
+// owns 32 rows (queries in the dQ kernel, keys in the dK/dV kernel) whose
+// operand fragments stay in VGPRs; the streamed tiles (32 rows) go HBM -> LDS by
+// buffer_load ... lds, stored once per way they are read: "row" layout for
+// ds_read_b128 fragments whose k index is the head dimension, "transposed"
+// layout for ds_read_b64_tr_b16 fragments whose k index is the row.
+//   dQ kernel, per K/V tile:   S^T = K Q^T, dP^T = V dO^T  (lane = query)
+//                              dQ^T += K^T dS^T
+//   dK/dV kernel, per Q tile:  S = Q K^T, dP = dO V^T      (lane = key)
+//                              dV^T += dO^T P,  dK^T += Q^T dS
+// P and dS are rounded (nearest-even) to the input type for the MFMAs that
+// consume them, as the forward rounds P.
+#pragma once
+
+#include "fa_mfma.hpp"
+
+namespace fa {
+
+template <int D_, bool CAUSAL_, int NW_>
+struct BwdConfig {
+    using L = MfmaConfig<D_, CAUSAL_, 1, NW_, 32>;  // staging of 32-row tiles, fragment offsets
+    static constexpr int D = D_, NW = NW_;
+    static constexpr bool CAUSAL = CAUSAL_;
+    static constexpr int KS = L::KS, DB = L::DB, RB = L::RB, TILE = L::TILE;
+    static constexpr int NT = 64 * NW;
+    static constexpr int BM = 32 * NW;  // rows (queries or keys) per workgroup
+    // D = 128 keeps two accumulators of 64 registers each in the dK/dV kernel
+    static constexpr int OCC_DQ = 2;
+    static constexpr int OCC_KV = D == 128 ? 1 : 2;
+};
+
+// Sum over the eight element products of two packed operands, in fp32.
+template <typename T>
+__device__ __forceinline__ float dot8(u32x4 a, u32x4 b);
+
+template <>
+__device__ __forceinline__ float dot8<F16>(u32x4 a, u32x4 b) {
+    const f16x8 x = __builtin_bit_cast(f16x8, a), y = __builtin_bit_cast(f16x8, b);
+    float s = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s = __builtin_fmaf((float)x[e], (float)y[e], s);
+    return s;
+}
+
+template <>
+__device__ __forceinline__ float dot8<BF16>(u32x4 a, u32x4 b) {
+    const bf16x8 x = __builtin_bit_cast(bf16x8, a), y = __builtin_bit_cast(bf16x8, b);
+    float s = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s = __builtin_fmaf((float)x[e], (float)y[e], s);
+    return s;
+}
+
+// Operand fragments of one row of a [S,D] head: lane (n, h) gets
+// X[row][16ks + 8h .. +7] for every k-step ks (row clamped to S-1).
+template <int KS>
+__device__ __forceinline__ void row_frags(const uint16_t* xh, int row, int D, int h, u32x4 (&f)[KS]) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        f[ks] = *reinterpret_cast<const u32x4*>(xh + (int64_t)row * D + ks * 16 + h * 8);
+        pin(f[ks]);
+    }
+}
+
+// LDS byte offsets of a lane's fragment reads (the forward's formulas): row
+// reads of chunk (2ks + h), and the transposed reads of dims 32db + ...
+template <typename Cfg>
+__device__ __forceinline__ void frag_offsets(int lane, int (&offk)[Cfg::KS], int (&offv)[Cfg::DB]) {
+    constexpr int D = Cfg::D, RB = Cfg::RB;
+    const int n = lane & 31, h = lane >> 5;
+#pragma unroll
+    for (int ks = 0; ks < Cfg::KS; ++ks) offk[ks] = n * RB + (((2 * ks + h) ^ swz_k<D>(n)) * 16);
+    const int r16 = lane & 15, g16 = lane >> 4;
+    const int vrow = 4 * h + (r16 >> 2);
+#pragma unroll
+    for (int db = 0; db < Cfg::DB; ++db) {
+        const int dim = (32 * db + 16 * (g16 & 1) + 4 * (r16 & 3)) % D;
+        offv[db] = vrow * RB + (((dim >> 3) ^ swz_v<D>(vrow)) * 16) + (dim & 7) * 2;
+    }
+}
+
+// Store a 32-row block held as X^T accumulators (rows = dims 32db + 8g + 4h +
+// 0..3, lane column = row of X), times `mul`, rounded to T.
+template <typename T, int D, int DB>
+__device__ __forceinline__ void store_t(uint16_t* xh, int row, int h, const f32x16 (&acc)[DB], float mul) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int d = db * 32 + 8 * g + 4 * h;
+            if (d < D) {
+                u32x2 w;
+                w[0] = pack2<T>(acc[db][4 * g + 0] * mul, acc[db][4 * g + 1] * mul);
+                w[1] = pack2<T>(acc[db][4 * g + 2] * mul, acc[db][4 * g + 3] * mul);
+                *reinterpret_cast<u32x2*>(xh + (int64_t)row * D + d) = w;
+            }
+        }
+}
+
+// ------------------------------------------------------------------ dQ kernel
+
+template <typename T, typename Cfg>
+__global__ __attribute__((amdgpu_flat_work_group_size(Cfg::NT, Cfg::NT), amdgpu_waves_per_eu(Cfg::OCC_DQ, Cfg::OCC_DQ)))
+void fa_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                      const uint16_t* __restrict__ V, const uint16_t* __restrict__ O,
+                      const uint16_t* __restrict__ dO, const float* __restrict__ LSE,
+                      uint16_t* __restrict__ dQ, float* __restrict__ DELTA, int S, int BH, int n_blk, float c,
+                      float scale) {
+    using L = typename Cfg::L;
+    using W = WaveTile<T, L>;
+    constexpr int D = Cfg::D, KS = Cfg::KS, DB = Cfg::DB, RB = Cfg::RB, BM = Cfg::BM;
+    constexpr bool CAUSAL = Cfg::CAUSAL;
+
+    // per K/V tile: K row layout (S^T operand), K transposed layout (dQ^T
+    // operand), V row layout (dP^T operand); two buffers each
+    __shared__ __attribute__((aligned(1024))) char kr0[Cfg::TILE];
+    __shared__ __attribute__((aligned(1024))) char kr1[Cfg::TILE];
+    __shared__ __attribute__((aligned(1024))) char kt0[Cfg::TILE];
+    __shared__ __attribute__((aligned(1024))) char kt1[Cfg::TILE];
+    __shared__ __attribute__((aligned(1024))) char vr0[Cfg::TILE];
+    __shared__ __attribute__((aligned(1024))) char vr1[Cfg::TILE];
+    FA_LDS char* const krb[2] = {(FA_LDS char*)kr0, (FA_LDS char*)kr1};
+    FA_LDS char* const ktb[2] = {(FA_LDS char*)kt0, (FA_LDS char*)kt1};
+    FA_LDS char* const vrb[2] = {(FA_LDS char*)vr0, (FA_LDS char*)vr1};
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n = lane & 31;
+    const int h = lane >> 5;
+
+    // heads vary fastest; causal query blocks longest first
+    const int wg = blockIdx.x;
+    const int bh = wg % BH;
+    const int rank = wg / BH;
+    const int qblk = CAUSAL ? (n_blk - 1 - rank) : rank;
+    const int q0 = qblk * BM;
+    const int qw = q0 + 32 * wave;
+
+    const int64_t head = (int64_t)bh * S * D;
+    const __amdgpu_buffer_rsrc_t krs = head_rsrc<T>(K + head, S * RB);
+    const __amdgpu_buffer_rsrc_t vrs = head_rsrc<T>(V + head, S * RB);
+    const uint32_t roff = tile_lane_offset<L, false>(wave, lane);
+    const uint32_t toff = tile_lane_offset<L, true>(wave, lane);
+
+    const int ntiles = ((CAUSAL ? min(q0 + BM, S) : S) + 31) / 32;
+    const int wt = qw < S ? min(ntiles, ((CAUSAL ? min(qw + 32, S) : S) + 31) / 32) : 0;
+    const int um = min(CAUSAL ? (qw + 1) / 32 : ntiles, S / 32);
+    const int qrow = min(qw + n, S - 1);
+    const int last = CAUSAL ? qrow : S - 1;
+
+    auto stage = [&](auto par, int t) __attribute__((always_inline)) {
+        constexpr int P = decltype(par)::value;
+        load_tile<T, L, false>(krb[P], krs, roff, t * 32, wave, lane);
+        load_tile<T, L, true>(ktb[P], krs, toff, t * 32, wave, lane);
+        load_tile<T, L, false>(vrb[P], vrs, roff, t * 32, wave, lane);
+    };
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    if (ntiles > 0) stage(P0{}, 0);
+
+    // resident: Q and dO fragments of the wave's 32 queries; D = rowsum(dO o O)
+    u32x4 qf[KS], df[KS];
+    row_frags<KS>(Q + head, qrow, D, h, qf);
+    row_frags<KS>(dO + head, qrow, D, h, df);
+    float delta;
+    {
+        u32x4 of[KS];
+        row_frags<KS>(O + head, qrow, D, h, of);
+        float part = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) part += dot8<T>(df[ks], of[ks]);
+        delta = halves_sum(part);
+    }
+    if (h == 0 && qw + n < S) DELTA[(int64_t)bh * S + qw + n] = delta;
+    const float lse2 = LSE[(int64_t)bh * S + qrow] * kLog2e;
+
+    int offk[KS], offv[DB];
+    frag_offsets<L>(lane, offk, offv);
+
+    f32x16 dqacc[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dqacc[db][r] = 0.f;
+
+    auto step = [&](auto par, int t) __attribute__((always_inline)) {
+        constexpr int P = decltype(par)::value;
+        wait_vmcnt0();
+        __syncthreads();
+        if (t + 1 < ntiles) stage(std::integral_constant<int, 1 - P>{}, t + 1);
+        if (t >= wt) return;
+        const f32x16 zero = {};
+        f32x16 st = zero, dpt = zero;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            st = mfma32x32x16<T>(W::k_frag(krb[P], offk, 0, ks), qf[ks], ks == 0 ? zero : st);
+            dpt = mfma32x32x16<T>(W::k_frag(vrb[P], offk, 0, ks), df[ks], ks == 0 ? zero : dpt);
+        }
+        if (t >= um) {
+            // key of register r: 32t + 8(r/4) + 4h + r%4, visible iff <= last
+            const int lim = last - (t * 32 + 4 * h);
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                if (8 * (r >> 2) + (r & 3) > lim) st[r] = kNegInf;
+        }
+        u32x4 dsp[2];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float p0 = exp2_fast(__builtin_fmaf(st[2 * i], c, -lse2));
+            const float p1 = exp2_fast(__builtin_fmaf(st[2 * i + 1], c, -lse2));
+            dsp[i >> 2][i & 3] = pack2<T>(p0 * (dpt[2 * i] - delta), p1 * (dpt[2 * i + 1] - delta));
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+                dqacc[db] = mfma32x32x16<T>(W::v_frag(ktb[P], offv, 0, j, db), dsp[j], dqacc[db]);
+    };
+    int t = 0;
+    for (; t + 1 < ntiles; t += 2) {
+        step(P0{}, t);
+        step(P1{}, t + 1);
+    }
+    if (t < ntiles) step(P0{}, t);
+
+    if (qw + n < S) store_t<T, D, DB>(dQ + head, qw + n, h, dqacc, scale);
+}
+
+// ---------------------------------------------------------------- dK/dV kernel
+
+template <typename T, typename Cfg>
+__global__ __attribute__((amdgpu_flat_work_group_size(Cfg::NT, Cfg::NT), amdgpu_waves_per_eu(Cfg::OCC_KV, Cfg::OCC_KV)))
+void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                        const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+                        const float* __restrict__ LSE, const float* __restrict__ DELTA,
+                        uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int S, int BH, int n_blk, float scale) {
+    using L = typename Cfg::L;
+    using W = WaveTile<T, L>;
+    constexpr int D = Cfg::D, KS = Cfg::KS, DB = Cfg::DB, RB = Cfg::RB, BM = Cfg::BM;
+    constexpr bool CAUSAL = Cfg::CAUSAL;
+
+    // per Q/dO tile: Q row layout (S operand), Q transposed layout (dK^T
+    // operand), dO row layout (dP operand), dO transposed layout (dV^T
+    // operand), and the tile's 32 lse and D values; two buffers each
+    __shared__ __attribute__((aligned(1024))) char qr0[Cfg::TILE];
+    __shared__ __attribute__((aligned(1024))) char qr1[Cfg::TILE];
+    __shared__ __attribute__((aligned(1024))) char qt0[Cfg::TILE];
+    __shared__ __attribute__((aligned(1024))) char qt1[Cfg::TILE];
+    __shared__ __attribute__((aligned(1024))) char or0[Cfg::TILE];
+    __shared__ __attribute__((aligned(1024))) char or1[Cfg::TILE];
+    __shared__ __attribute__((aligned(1024))) char ot0[Cfg::TILE];
+    __shared__ __attribute__((aligned(1024))) char ot1[Cfg::TILE];
+    __shared__ __attribute__((aligned(16))) float ls0[32];
+    __shared__ __attribute__((aligned(16))) float ls1[32];
+    __shared__ __attribute__((aligned(16))) float dl0[32];
+    __shared__ __attribute__((aligned(16))) float dl1[32];
+    FA_LDS char* const qrb[2] = {(FA_LDS char*)qr0, (FA_LDS char*)qr1};
+    FA_LDS char* const qtb[2] = {(FA_LDS char*)qt0, (FA_LDS char*)qt1};
+    FA_LDS char* const orb[2] = {(FA_LDS char*)or0, (FA_LDS char*)or1};
+    FA_LDS char* const otb[2] = {(FA_LDS char*)ot0, (FA_LDS char*)ot1};
+    FA_LDS float* const lsb[2] = {(FA_LDS float*)ls0, (FA_LDS float*)ls1};
+    FA_LDS float* const dlb[2] = {(FA_LDS float*)dl0, (FA_LDS float*)dl1};
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n = lane & 31;
+    const int h = lane >> 5;
+
+    // heads vary fastest; causal key blocks with the most queries (lowest
+    // keys) first
+    const int wg = blockIdx.x;
+    const int bh = wg % BH;
+    const int kblk = wg / BH;
+    const int k0 = kblk * BM;
+    const int kw = k0 + 32 * wave;
+
+    const int64_t head = (int64_t)bh * S * D;
+    const __amdgpu_buffer_rsrc_t qrs = head_rsrc<T>(Q + head, S * RB);
+    const __amdgpu_buffer_rsrc_t ors = head_rsrc<T>(dO + head, S * RB);
+    const uint32_t roff = tile_lane_offset<L, false>(wave, lane);
+    const uint32_t toff = tile_lane_offset<L, true>(wave, lane);
+
+    const int nq = (S + 31) / 32;                    // query tiles of the head
+    const int t0 = CAUSAL ? k0 / 32 : 0;             // first query tile any key here sees
+    const int tw = CAUSAL ? kw / 32 : 0;             // this wave's first query tile
+    const bool live = kw < S;                        // the wave has keys
+    const bool ragged = (S % 32) != 0;               // last query tile has rows past S
+
+    auto stage = [&](auto par, int t) __attribute__((always_inline)) {
+        constexpr int P = decltype(par)::value;
+        load_tile<T, L, false>(qrb[P], qrs, roff, t * 32, wave, lane);
+        load_tile<T, L, true>(qtb[P], qrs, toff, t * 32, wave, lane);
+        load_tile<T, L, false>(orb[P], ors, roff, t * 32, wave, lane);
+        load_tile<T, L, true>(otb[P], ors, toff, t * 32, wave, lane);
+    };
+    // A tile's 32 lse and D values go through lanes 0..31 of wave 0: loaded
+    // into registers one tile ahead, written to LDS (plain stores) after the
+    // next wait, before the barrier that publishes the tile.  Rows past S get
+    // 0 and are masked.
+    float lreg = 0.f, dreg = 0.f;
+    const bool ld_lane = wave == 0 && lane < 32;
+    auto fetch_ld = [&](int t) __attribute__((always_inline)) {
+        const int row = t * 32 + lane;
+        if (ld_lane && row < S) {
+            lreg = LSE[(int64_t)bh * S + row];
+            dreg = DELTA[(int64_t)bh * S + row];
+        } else {
+            lreg = 0.f;
+            dreg = 0.f;
+        }
+    };
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    if (t0 < nq) {
+        stage(P0{}, t0);
+        fetch_ld(t0);
+    }
+
+    // resident: K and V fragments of the wave's 32 keys
+    const int krow = min(kw + n, S - 1);
+    u32x4 kf[KS], vf[KS];
+    row_frags<KS>(K + head, krow, D, h, kf);
+    row_frags<KS>(V + head, krow, D, h, vf);
+
+    int offk[KS], offv[DB];
+    frag_offsets<L>(lane, offk, offv);
+
+    f32x16 dkacc[DB], dvacc[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            dkacc[db][r] = 0.f;
+            dvacc[db][r] = 0.f;
+        }
+
+    // query tile t, buffers of parity (t - t0) % 2
+    auto step = [&](auto par, int t) __attribute__((always_inline)) {
+        constexpr int P = decltype(par)::value;
+        wait_vmcnt0();
+        if (ld_lane) {
+            lsb[P][lane] = lreg;
+            dlb[P][lane] = dreg;
+        }
+        __syncthreads();
+        if (t + 1 < nq) {
+            stage(std::integral_constant<int, 1 - P>{}, t + 1);
+            fetch_ld(t + 1);
+        }
+        if (!live || t < tw) return;
+        const f32x16 zero = {};
+        f32x16 s = zero, dp = zero;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            s = mfma32x32x16<T>(W::k_frag(qrb[P], offk, 0, ks), kf[ks], ks == 0 ? zero : s);
+            dp = mfma32x32x16<T>(W::k_frag(orb[P], offk, 0, ks), vf[ks], ks == 0 ? zero : dp);
+        }
+        // query of register r: 32t + 8(r/4) + 4h + r%4; lse and D for the four
+        // consecutive queries of each register group come in one 16-byte read
+        float lse[16], dd[16];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            // (read as a float vector: a bit_cast of a vector-element lvalue
+            // yields element 0 with this compiler)
+            const f32x4 a = *reinterpret_cast<const FA_LDS f32x4*>(lsb[P] + 8 * g + 4 * h);
+            const f32x4 b = *reinterpret_cast<const FA_LDS f32x4*>(dlb[P] + 8 * g + 4 * h);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                lse[4 * g + e] = a[e];
+                dd[4 * g + e] = b[e];
+            }
+        }
+        // visible iff query >= key (causal, only the diagonal tile t == tw
+        // has both) and query < S (only the last tile when S % 32 != 0)
+        const bool diag = CAUSAL && t == tw;
+        const bool tail = ragged && t == nq - 1;
+        u32x4 pp[2], dsp[2];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            float pv[2], dv[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int r = 2 * i + e;
+                const int rr = 8 * (r >> 2) + 4 * h + (r & 3);
+                const bool hide = (diag & (rr < n)) | (tail & (t * 32 + rr >= S));
+                const float p = hide ? 0.f : exp2_fast(kLog2e * __builtin_fmaf(s[r], scale, -lse[r]));
+                pv[e] = p;
+                dv[e] = p * (dp[r] - dd[r]);
+            }
+            pp[i >> 2][i & 3] = pack2<T>(pv[0], pv[1]);
+            dsp[i >> 2][i & 3] = pack2<T>(dv[0], dv[1]);
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                dvacc[db] = mfma32x32x16<T>(W::v_frag(otb[P], offv, 0, j, db), pp[j], dvacc[db]);
+                dkacc[db] = mfma32x32x16<T>(W::v_frag(qtb[P], offv, 0, j, db), dsp[j], dkacc[db]);
+            }
+    };
+    int t = t0;
+    for (; t + 1 < nq; t += 2) {
+        step(P0{}, t);
+        step(P1{}, t + 1);
+    }
+    if (t < nq) step(P0{}, t);
+
+    if (live && kw + n < S) {
+        store_t<T, D, DB>(dK + head, kw + n, h, dkacc, scale);
+        store_t<T, D, DB>(dV + head, kw + n, h, dvacc, 1.0f);
+    }
+}
+
+}  // namespace fa

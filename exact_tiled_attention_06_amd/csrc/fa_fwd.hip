@@ -16,6 +16,7 @@
 #include "fa_mfma.hpp"
 #include "fa_ksplit.hpp"
 #include "fa_split.hpp"
+#include "fa_bwd.hpp"
 
 #ifndef FA_SPLIT_TBN
 #define FA_SPLIT_TBN 128
@@ -140,21 +141,106 @@ int dispatch_d(int64_t D, int dtype, const void* q, const void* k, const void* v
     }
 }
 
-}  // namespace
+// ------------------------------------------------------------------ backward
 
-extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
-                      int64_t H, int64_t S, int64_t D, int causal, float scale, int dtype,
-                      void* stream) {
-    // ---- argument checks: no HIP call before all of them pass ----------------
+template <typename T, int D, bool CAUSAL>
+int launch_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+               void* dq, void* dk, void* dv, float* delta, int S, int BH, float c, float scale,
+               hipStream_t stream) {
+    using Cfg = BwdConfig<D, CAUSAL, 4>;
+    const int n_blk = (S + Cfg::BM - 1) / Cfg::BM;
+    const int64_t grid = (int64_t)n_blk * BH;
+    if (grid > (int64_t)1 << 24) return FA_ERR_TOO_LARGE;
+    (void)hipGetLastError();
+    // dQ (and D = rowsum(dO o O) into `delta`), then dK and dV, which read D
+    hipLaunchKernelGGL((fa_bwd_dq_kernel<T, Cfg>), dim3((unsigned)grid), dim3(Cfg::NT), 0, stream,
+                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)o,
+                       (const uint16_t*)dout, lse, (uint16_t*)dq, delta, S, BH, n_blk, c, scale);
+    if (hipGetLastError() != hipSuccess) return FA_ERR_LAUNCH;
+    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<T, Cfg>), dim3((unsigned)grid), dim3(Cfg::NT), 0, stream,
+                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, lse,
+                       (const float*)delta, (uint16_t*)dk, (uint16_t*)dv, S, BH, n_blk, scale);
+    return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+template <bool CAUSAL>
+int dispatch_bwd(int64_t D, int dtype, const void* q, const void* k, const void* v, const void* o,
+                 const void* dout, const float* lse, void* dq, void* dk, void* dv, float* delta, int S, int BH,
+                 float c, float scale, hipStream_t st) {
+#define FA_BWD_CASE(DD)                                                                                   \
+    case DD:                                                                                              \
+        return dtype == FA_DTYPE_F16                                                                      \
+                   ? launch_bwd<F16, DD, CAUSAL>(q, k, v, o, dout, lse, dq, dk, dv, delta, S, BH, c, scale, st) \
+                   : launch_bwd<BF16, DD, CAUSAL>(q, k, v, o, dout, lse, dq, dk, dv, delta, S, BH, c, scale, st);
+    switch (D) {
+        FA_BWD_CASE(16)
+        FA_BWD_CASE(32)
+        FA_BWD_CASE(64)
+        default: FA_BWD_CASE(128)
+    }
+#undef FA_BWD_CASE
+}
+
+// Checks shared by both entry points (no HIP call).
+int check_problem(int64_t B, int64_t H, int64_t S, int64_t D, int causal, float scale) {
     if (B < 0 || H < 0 || S < 0) return FA_ERR_SHAPE;
     if (D != 16 && D != 32 && D != 64 && D != 128) return FA_ERR_HEAD_DIM;
-    if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
     if (causal != 0 && causal != 1) return FA_ERR_CAUSAL;
     // finite and > 0, tested on the bits (the library is built without NaN semantics)
     uint32_t sbits;
     memcpy(&sbits, &scale, sizeof sbits);
     if (((sbits >> 23) & 0xFFu) == 0xFFu || (sbits >> 31) != 0u || (sbits & 0x7FFFFFFFu) == 0u)
         return FA_ERR_SCALE;
+    return FA_OK;
+}
+
+}  // namespace
+
+extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                      const float* lse, void* dq, void* dk, void* dv, float* delta, int64_t B, int64_t H,
+                      int64_t S, int64_t D, int causal, float scale, int dtype, void* stream) {
+    // ---- argument checks: no HIP call before all of them pass ----------------
+    int rc = check_problem(B, H, S, D, causal, scale);
+    if (rc == FA_ERR_SHAPE || rc == FA_ERR_HEAD_DIM) return rc;
+    if (dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
+    if (rc != FA_OK) return rc;
+    if (B == 0 || H == 0 || S == 0) return FA_OK;
+    if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !delta) return FA_ERR_NULL_POINTER;
+    const int64_t kMaxInt = 2147483647;
+    if (B > kMaxInt || H > kMaxInt || B * H > kMaxInt / 2 || S > (kMaxInt >> 1)) return FA_ERR_TOO_LARGE;
+    const int64_t BH = B * H;
+    if (BH > INT64_MAX / S || BH * S > INT64_MAX / (D * 8)) return FA_ERR_TOO_LARGE;
+    if (S * D * 2 > kMaxInt) return FA_ERR_TOO_LARGE;
+    const int64_t tb = BH * S * D * 2, vb = BH * S * 4;
+    if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)dout | (uintptr_t)dq |
+         (uintptr_t)dk | (uintptr_t)dv) & 15)
+        return FA_ERR_ALIGNMENT;
+    if (((uintptr_t)lse | (uintptr_t)delta) & 3) return FA_ERR_ALIGNMENT;
+    // every output (dq, dk, dv, delta) apart from every other buffer
+    const void* outs[4] = {dq, dk, dv, delta};
+    const int64_t out_bytes[4] = {tb, tb, tb, vb};
+    const void* all[10] = {q, k, v, o, dout, lse, dq, dk, dv, delta};
+    const int64_t all_bytes[10] = {tb, tb, tb, tb, tb, vb, tb, tb, tb, vb};
+    for (int i = 0; i < 4; ++i)
+        for (int j = 0; j < 10; ++j)
+            if (j != 6 + i && overlaps(outs[i], out_bytes[i], all[j], all_bytes[j])) return FA_ERR_ALIAS;
+
+    const float c = (float)((double)scale * 1.4426950408889634);
+    hipStream_t st = (hipStream_t)stream;
+    return causal ? dispatch_bwd<true>(D, dtype, q, k, v, o, dout, lse, dq, dk, dv, delta, (int)S, (int)BH, c,
+                                       scale, st)
+                  : dispatch_bwd<false>(D, dtype, q, k, v, o, dout, lse, dq, dk, dv, delta, (int)S, (int)BH, c,
+                                        scale, st);
+}
+
+extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                      int64_t H, int64_t S, int64_t D, int causal, float scale, int dtype,
+                      void* stream) {
+    // ---- argument checks: no HIP call before all of them pass ----------------
+    int rc = check_problem(B, H, S, D, causal, scale);
+    if (rc == FA_ERR_SHAPE || rc == FA_ERR_HEAD_DIM) return rc;
+    if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
+    if (rc != FA_OK) return rc;
     if (B == 0 || H == 0 || S == 0) return FA_OK;  // empty problem: nothing to compute
     if (!q || !k || !v || !o || !lse) return FA_ERR_NULL_POINTER;
     // index ranges: heads*S must fit the kernels' int arithmetic, S*D per head int64
@@ -191,7 +277,7 @@ extern "C" const char* fa_status_string(int status) {
         case FA_ERR_DTYPE: return "dtype must be FA_DTYPE_F32, FA_DTYPE_F16 or FA_DTYPE_BF16";
         case FA_ERR_CAUSAL: return "causal must be 0 or 1";
         case FA_ERR_SCALE: return "scale must be finite and > 0";
-        case FA_ERR_ALIAS: return "o and lse must not overlap each other or q, k, v";
+        case FA_ERR_ALIAS: return "outputs must not overlap each other or the inputs";
         case FA_ERR_TOO_LARGE: return "problem size exceeds the kernels' index ranges";
         case FA_ERR_LAUNCH: return "the HIP runtime rejected the kernel launch";
         case FA_ERR_ALIGNMENT: return "q, k, v, o must be 16-byte aligned and lse 4-byte aligned";

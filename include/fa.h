@@ -1,5 +1,6 @@
 /*
- * fa.h -- FlashAttention-2 forward pass for AMD Instinct MI355X (gfx950).
+ * fa.h -- FlashAttention-2 forward and backward passes for AMD Instinct
+ * MI355X (gfx950).
  *
  * One call computes exact attention for every (batch, head):
  *
@@ -43,14 +44,14 @@ extern "C" {
 #define FA_ERR_NULL_POINTER 1   /* a tensor pointer is NULL for a non-empty problem */
 #define FA_ERR_SHAPE 2          /* B, H or S is negative */
 #define FA_ERR_HEAD_DIM 3       /* D is not 16, 32, 64 or 128 */
-#define FA_ERR_DTYPE 4          /* dtype is not FA_DTYPE_F32 / _F16 / _BF16 */
+#define FA_ERR_DTYPE 4          /* dtype is not FA_DTYPE_F32 / _F16 / _BF16 (fa_bwd: _F16 / _BF16) */
 #define FA_ERR_CAUSAL 5         /* causal is not 0 or 1 */
 #define FA_ERR_SCALE 6          /* scale is not finite or not > 0 */
-#define FA_ERR_ALIAS 7          /* o or lse overlaps q, k, v or each other */
+#define FA_ERR_ALIAS 7          /* an output overlaps another output or an input */
 #define FA_ERR_TOO_LARGE 8      /* sizes overflow the kernels' index ranges (for fp16 / bf16
                                    also: one head's K or V, S * D * 2 bytes, must be < 2^31) */
 #define FA_ERR_LAUNCH 9         /* the HIP runtime rejected the kernel launch */
-#define FA_ERR_ALIGNMENT 10     /* q, k, v, o not 16-byte aligned, or lse not 4-byte aligned */
+#define FA_ERR_ALIGNMENT 10     /* a [B,H,S,D] tensor not 16-byte aligned, or lse / delta not 4-byte aligned */
 
 /* ---- element types (the dtype argument) --------------------------------- */
 #define FA_DTYPE_F32 0
@@ -89,6 +90,50 @@ extern "C" {
  * surface on the stream, as for any kernel.
  */
 int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
+           int64_t B, int64_t H, int64_t S, int64_t D,
+           int causal, float scale, int dtype, void *stream);
+
+/*
+ * fa_bwd -- gradients of the attention above for an upstream gradient dO of O.
+ *
+ * With P = exp(scale * Q K^T - lse) recomputed from the saved lse (masked
+ * keys get 0), D_i = rowsum(dO_i o O_i) and dS = P o (dO V^T - D):
+ *
+ *     dQ = scale * dS K,   dK = scale * dS^T Q,   dV = P^T dO
+ *
+ * ("从零训练语言模型（第二部分）", sections "使用 LSE 连接正向和反向传播" and
+ * "反向传播": recompute P from lse, then dV, dP, dS, dQ and dK; the CS336
+ * write-up, problem flash_backward, for the same equations with the scale.)
+ *
+ *   q, k, v, o, dout  device pointers to contiguous [B,H,S,D] tensors of
+ *                     `dtype` (16-byte aligned): the forward's inputs, its
+ *                     output O and the upstream gradient dO.  They may alias
+ *                     one another.
+ *   lse               device pointer to the forward's float32 [B,H,S] lse
+ *                     (natural log), 4-byte aligned.
+ *   dq, dk, dv        device pointers to contiguous [B,H,S,D] outputs of
+ *                     `dtype` (16-byte aligned), fully written.
+ *   delta             device workspace of B*H*S floats (4-byte aligned): the
+ *                     call writes D_i there before it reads it; its content
+ *                     afterwards is D.
+ *   B, H, S, D, causal, scale, stream   as for fa_fwd (the same values the
+ *                     forward was called with).
+ *   dtype             FA_DTYPE_F16 or FA_DTYPE_BF16 (fp32 is not supported by
+ *                     the backward: FA_ERR_DTYPE).  The products run on the
+ *                     matrix cores with fp32 accumulation; P and dS are
+ *                     rounded (nearest-even) to dtype before the products
+ *                     that consume them; the outputs are rounded to dtype.
+ *
+ * Ownership: the caller allocates all ten buffers; dq, dk, dv and delta must
+ * not overlap each other or any input.  Two kernels are enqueued on `stream`
+ * (dQ and D, then dK and dV) and the call returns at once; nothing is
+ * allocated, freed or synchronised.
+ *
+ * Errors: as for fa_fwd (checks before any HIP call, the first failed check's
+ * code, nothing written), with FA_ERR_DTYPE also for FA_DTYPE_F32.
+ */
+int fa_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout,
+           const float *lse, void *dq, void *dk, void *dv, float *delta,
            int64_t B, int64_t H, int64_t S, int64_t D,
            int causal, float scale, int dtype, void *stream);
 

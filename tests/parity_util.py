@@ -8,6 +8,14 @@ design notes):
   lse, all dtypes: max |lse_gpu - lse_ref| / max |lse_ref| <= 1e-4 and, per element,
                    |lse_gpu - lse_ref| <= 1e-4 * max(|lse_ref|, 1)
 O_ref and lse_ref are the unrounded float64 oracle values on the same stored inputs.
+
+Gradients (dQ, dK, dV of the backward), normwise:
+  max |g_gpu - g_ref| / max(max |g_ref|, 1e-2) <= 4u,  u = 2^-11 (fp16), 2^-8 (bf16):
+  the output rounding contributes at most u/2, the rounding of P and dS to the
+  input type before their products about u (1.5u worst in a CPU emulation of the
+  kernels' arithmetic on the parity shapes), the fp32 parts ~1e-6.  The floor
+  holds a gradient that vanishes in exact arithmetic (dQ and dK at S = 1) to an
+  absolute bound instead of a ratio to zero.
 """
 from __future__ import annotations
 
@@ -17,6 +25,9 @@ import torch
 O_ABS_TOL = {"f16": 5e-3, "bf16": 2e-2}
 O_REL_TOL_F32 = 1e-4
 LSE_REL_TOL = 1e-4
+
+GRAD_REL_TOL = {"f16": 4 * 2.0 ** -11, "bf16": 4 * 2.0 ** -8}
+GRAD_FLOOR = 1e-2
 
 DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 
@@ -46,6 +57,22 @@ def check_o(o_gpu: np.ndarray, o_ref: np.ndarray, dtype: str, what: str = "O") -
         raise AssertionError(f"{what}: max abs error {err:.3e} > {tol} at {idx}: "
                              f"gpu {o_gpu[idx]!r} ref {o_ref[idx]!r}")
     return err
+
+
+def check_grad(g_gpu: np.ndarray, g_ref: np.ndarray, dtype: str, what: str = "grad") -> float:
+    assert g_gpu.shape == g_ref.shape, f"{what}: shape {g_gpu.shape} vs {g_ref.shape}"
+    assert np.all(np.isfinite(g_gpu)), f"{what}: non-finite GPU values"
+    if g_gpu.size == 0:
+        return 0.0
+    ref_max = float(np.max(np.abs(g_ref)))
+    err = float(np.max(np.abs(g_gpu - g_ref)))
+    rel = err / max(ref_max, GRAD_FLOOR)
+    tol = GRAD_REL_TOL[dtype]
+    if rel > tol:
+        idx = np.unravel_index(np.argmax(np.abs(g_gpu - g_ref)), g_gpu.shape)
+        raise AssertionError(f"{what}: normwise error {rel:.3e} > {tol:.3e} (max |ref| {ref_max:.3e}) "
+                             f"at {idx}: gpu {g_gpu[idx]!r} ref {g_ref[idx]!r}")
+    return rel
 
 
 def check_lse(l_gpu: np.ndarray, l_ref: np.ndarray, what: str = "lse") -> float:

@@ -125,3 +125,57 @@ def test_python_errors_map(fa):
     with pytest.raises(RuntimeError):
         fa.check(fa.FA_ERR_LAUNCH)
     fa.check(fa.FA_OK)
+
+
+# ---- fa_bwd: the same checks, over its ten buffers
+BARGS = dict(q=P, k=2 * P, v=3 * P, o=4 * P, dout=5 * P, lse=6 * P, dq=7 * P, dk=8 * P, dv=9 * P,
+             delta=10 * P, B=1, H=1, S=64, D=64, causal=0, scale=0.125, dtype=1, stream=0)
+
+
+def bcall(fa, **over):
+    a = dict(BARGS, **over)
+    return fa.fa_bwd(a["q"], a["k"], a["v"], a["o"], a["dout"], a["lse"], a["dq"], a["dk"], a["dv"],
+                     a["delta"], a["B"], a["H"], a["S"], a["D"], a["causal"], a["scale"], a["dtype"],
+                     a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(B=-1), "FA_ERR_SHAPE"),
+    (dict(D=96), "FA_ERR_HEAD_DIM"),
+    (dict(dtype=0), "FA_ERR_DTYPE"),              # fp32 has no backward
+    (dict(dtype=5), "FA_ERR_DTYPE"),
+    (dict(causal=-1), "FA_ERR_CAUSAL"),
+    (dict(scale=float("nan")), "FA_ERR_SCALE"),
+    (dict(dout=0), "FA_ERR_NULL_POINTER"),
+    (dict(delta=0), "FA_ERR_NULL_POINTER"),
+    (dict(dv=0), "FA_ERR_NULL_POINTER"),
+    (dict(dq=P), "FA_ERR_ALIAS"),                  # dq == q
+    (dict(dk=7 * P + 512), "FA_ERR_ALIAS"),        # dk inside dq
+    (dict(delta=6 * P + 64), "FA_ERR_ALIAS"),      # delta inside lse
+    (dict(delta=9 * P + 4), "FA_ERR_ALIAS"),       # delta inside dv (and 4-byte aligned)
+    (dict(dv=5 * P), "FA_ERR_ALIAS"),              # dv == dout
+    (dict(dout=5 * P + 8), "FA_ERR_ALIGNMENT"),
+    (dict(dk=8 * P + 4), "FA_ERR_ALIGNMENT"),
+    (dict(delta=10 * P + 2), "FA_ERR_ALIGNMENT"),
+    (dict(S=1 << 23, D=128), "FA_ERR_TOO_LARGE"),
+])
+def test_bwd_rejects_bad_arguments(fa, over, code):
+    assert bcall(fa, **over) == _defines()[code]
+
+
+def test_bwd_first_failed_check_wins(fa):
+    assert bcall(fa, B=-1, D=48, dtype=0) == fa.FA_ERR_SHAPE
+    assert bcall(fa, D=48, dtype=0) == fa.FA_ERR_HEAD_DIM
+    assert bcall(fa, dtype=0, causal=3) == fa.FA_ERR_DTYPE
+
+
+@pytest.mark.parametrize("over", [dict(B=0), dict(H=0), dict(S=0)])
+def test_bwd_empty_problem_is_a_no_op(fa, over):
+    nulls = {n: 0 for n in ("q", "k", "v", "o", "dout", "lse", "dq", "dk", "dv", "delta")}
+    assert bcall(fa, **nulls, **over) == fa.FA_OK
+
+
+def test_bwd_inputs_may_alias(fa):
+    # q, k, v, o, dout share storage: only outputs are checked, so this fails
+    # at the null-pointer check that follows the input checks
+    assert bcall(fa, k=P, v=P, o=P, dout=P, delta=0) == fa.FA_ERR_NULL_POINTER

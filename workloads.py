@@ -73,6 +73,15 @@ def make_inputs(B: int, H: int, S: int, D: int, dtype: str, seed: int):
     return tuple(out)
 
 
+def make_grad(B: int, H: int, S: int, D: int, dtype: str, seed: int):
+    """An upstream gradient dO for the backward: randn [B,H,S,D] in float32 from
+    ``seed``, rounded to ``dtype`` (drawn apart from q, k, v)."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    x = torch.randn((B, H, S, D), dtype=torch.float32, generator=g)
+    return x.to(DTYPES[dtype]).contiguous()
+
+
 def workload_inputs(w: Workload):
     return make_inputs(w.B, w.H, w.S, w.D, w.dtype, w.seed)
 
