@@ -1,5 +1,5 @@
 #!/usr/bin/env python3
-"""Benchmark of the FlashAttention-2 forward on one MI355X.
+"""Benchmark of the FlashAttention-2 forward (and backward) on one MI355X.
 
 One step = one forward pass (one fa_fwd launch) over the multi-head causal
 workload B=4, H=16, S=4096, D=64, fp16, [B,H,S,D] layout, with q, k, v drawn
@@ -16,7 +16,11 @@ Prints one JSON line.  Also reported:
                 while the kernel sources still hash to what was profiled, else
                 null (--traffic-bytes overrides);
   cpu_baseline  the float64 CPU oracle timed on this host's cores over the
-                whole workload (every row of every head), in the same unit.
+                whole workload (every row of every head), in the same unit;
+  backward      fa_bwd (dQ, dK, dV) on the same workload with a seeded dO:
+                TFLOP/s with the usual 2.5x-forward FLOP count, HIP-event
+                kernel time, and the oracle's gradients over one head as its
+                CPU baseline (--no-backward skips it).
 
 Options: --gpus N (only 1 is supported: the kernel runs on one GPU),
 --steps K (timed launches), --warmup W, --workload NAME, --no-cpu-baseline,
@@ -80,6 +84,59 @@ def time_workload(fa, torch, w, causal, steps, warmup):
     return wall, kernel_ms
 
 
+def time_backward(fa, torch, w, causal, steps, warmup):
+    """HIP-event times of fa_bwd (dQ kernel, then dK/dV kernel) on the workload,
+    with the forward's O and lse and a seeded dO, outputs preallocated."""
+    import workloads
+    q, k, v = (x.to("cuda:0") for x in workloads.workload_inputs(w))
+    dout = workloads.make_grad(w.B, w.H, w.S, w.D, w.dtype, w.seed + 1000).to("cuda:0")
+    o, lse = fa.forward(q, k, v, causal=causal, scale=w.scale)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    delta = torch.empty((w.B, w.H, w.S), dtype=torch.float32, device="cuda:0")
+    stream = torch.cuda.current_stream()
+    ptrs = [t.data_ptr() for t in (q, k, v, o, dout, lse, dq, dk, dv, delta)]
+    code = fa.DTYPE_CODES[q.dtype]
+
+    def call():
+        return fa.fa_bwd(*ptrs, w.B, w.H, w.S, w.D, int(causal), w.scale, code, stream.cuda_stream)
+
+    fa.check(call())
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        call()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall, [s.elapsed_time(e) for s, e in zip(starts, ends)]
+
+
+def cpu_baseline_backward(w, causal):
+    """The float64 oracle's gradients over one head of the workload (a bounded sample)."""
+    import oracle
+    import workloads
+    orc = oracle.default()
+    q, k, v = (x[:1, :1].double().numpy() for x in workloads.workload_inputs(w))
+    dout = workloads.make_grad(w.B, w.H, w.S, w.D, w.dtype, w.seed + 1000)[:1, :1].double().numpy()
+    t0 = time.perf_counter()
+    orc.attention_bwd(q, k, v, dout, causal, w.scale)
+    dt = time.perf_counter() - t0
+    head_flops = 2.5 * w.flops(causal) / (w.B * w.H)
+    return {
+        "value": head_flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": orc.num_threads(),
+        "kind": "oracle",
+        "sample": f"one head of the workload ({w.S} rows, float64, {dt:.2f} s wall), "
+                  f"FLOPs counted as 2.5x the forward's",
+    }
+
+
 def cpu_baseline(w, causal):
     import numpy as np
     import oracle
@@ -106,6 +163,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="multihead_causal")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward measurement")
+    ap.add_argument("--traffic-bytes-bwd", type=float, default=None,
+                    help="HBM bytes per fa_bwd call measured with rocprofv3 counters")
     ap.add_argument("--traffic-bytes", type=float, default=None,
                     help="HBM bytes per launch measured with rocprofv3 counters")
     ap.add_argument("--sweep", default=None, help="write per-workload JSON lines to this file")
@@ -186,6 +246,34 @@ def main():
         },
         "cpu_baseline": None,
     }
+
+    if not args.no_backward and w.dtype in ("f16", "bf16"):
+        bwall, bms = time_backward(fa, torch, w, causal, args.steps, args.warmup)
+        bavg = sum(bms) / len(bms)
+        bflops = 2.5 * flops  # the usual count: five tile products to the forward's two
+        executed = 3.5 * flops  # S and dP are formed by both kernels: seven products
+        out["backward"] = {
+            "metric": "attention bwd TFLOP/s (dQ, dK, dV; FLOPs = 2.5x the forward's)",
+            "value": round(bflops / (bwall / args.steps) / 1e12, 2),
+            "unit": "TFLOP/s",
+            "ms_per_step": round(bwall * 1e3 / args.steps, 5),
+            "kernels": ["fa_bwd_dq_kernel", "fa_bwd_dkdv_kernel"],
+            "roofline": {
+                "bound": "mfma",
+                "achieved": round(bflops / (bavg * 1e-3) / 1e12, 2),
+                "achieved_executed": round(executed / (bavg * 1e-3) / 1e12, 2),
+                "peak": peak,
+                "unit": "TFLOP/s",
+                "frac": round(bflops / (bavg * 1e-3) / 1e12 / peak, 4),
+                "frac_executed": round(executed / (bavg * 1e-3) / 1e12 / peak, 4),
+                "traffic": args.traffic_bytes_bwd if args.traffic_bytes_bwd is not None
+                           else profiled_traffic(w.name + ":backward"),
+                "traffic_unit": "bytes per fa_bwd call (both kernels; HBM, rocprofv3 FETCH_SIZE + WRITE_SIZE)",
+                "kernel_ms_avg": round(bavg, 5),
+                "kernel_ms_min": round(min(bms), 5),
+            },
+            "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline_backward(w, causal),
+        }
 
     if args.sweep:
         with open(args.sweep, "w") as f:
