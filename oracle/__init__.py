@@ -53,24 +53,48 @@ def _as_f64(a) -> np.ndarray:
     return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
 
 
+def _shapes(q, k, v, extra=()):
+    """[B,H,S,D] queries, [B,Hkv,S,D] keys and values (H a multiple of Hkv)."""
+    if q.ndim != 4 or k.ndim != 4 or v.shape != k.shape:
+        raise ValueError(f"q must be [B,H,S,D] and k, v one [B,Hkv,S,D] shape, got {q.shape}, {k.shape}, {v.shape}")
+    B, H, S, D = q.shape
+    if k.shape[0] != B or k.shape[2:] != (S, D) or k.shape[1] < 1 or H % k.shape[1] != 0:
+        raise ValueError(f"k, v shape {k.shape} does not fit q {q.shape} (H must be a multiple of Hkv)")
+    for x in extra:
+        if x.shape != q.shape:
+            raise ValueError(f"expected shape {q.shape}, got {x.shape}")
+    return B, H, k.shape[1], S, D
+
+
+def _window(window):
+    wl, wr = (int(window[0]), int(window[1])) if window is not None else (-1, -1)
+    if wl < -1 or wr < -1:
+        raise ValueError(f"window bounds must be >= -1 (-1: unlimited), got {window}")
+    return wl, wr
+
+
 class Oracle:
-    """ctypes handle on one build of ``attn_oracle.c``."""
+    """ctypes handle on one build of ``attn_oracle.c``.
+
+    Keys and values may have fewer heads than the queries (grouped heads:
+    query head h reads key/value head h // (H // Hkv)); ``window = (left, right)``
+    limits query i to keys i - left .. i + right (-1: no limit on that side).
+    """
 
     def __init__(self, library: str):
         lib = ctypes.CDLL(library)
-        lib.oracle_attn_fwd.restype = ctypes.c_int
-        lib.oracle_attn_fwd.argtypes = [_c_double_p] * 5 + [ctypes.c_int64] * 4 + [
-            ctypes.c_int, ctypes.c_double]
-        lib.oracle_attn_fwd_rows.restype = ctypes.c_int
-        lib.oracle_attn_fwd_rows.argtypes = [_c_double_p] * 3 + [ctypes.c_int64] * 4 + [
-            ctypes.c_int, ctypes.c_double, _c_int64_p, ctypes.c_int64, _c_double_p, _c_double_p]
-        lib.oracle_attn_bwd.restype = ctypes.c_int
-        lib.oracle_attn_bwd.argtypes = [_c_double_p] * 7 + [ctypes.c_int64] * 4 + [
-            ctypes.c_int, ctypes.c_double]
-        lib.oracle_attn_bwd_rows.restype = ctypes.c_int
-        lib.oracle_attn_bwd_rows.argtypes = [_c_double_p] * 4 + [ctypes.c_int64] * 4 + [
-            ctypes.c_int, ctypes.c_double, _c_int64_p, ctypes.c_int64] + [_c_double_p] * 3
-        lib.oracle_num_threads.restype = ctypes.c_int
+        I64, I, D_ = ctypes.c_int64, ctypes.c_int, ctypes.c_double
+        lib.oracle_attn_fwd_ex.restype = I
+        lib.oracle_attn_fwd_ex.argtypes = [_c_double_p] * 5 + [I64] * 5 + [I, I64, I64, D_]
+        lib.oracle_attn_fwd_rows_ex.restype = I
+        lib.oracle_attn_fwd_rows_ex.argtypes = [_c_double_p] * 3 + [I64] * 5 + [I, I64, I64, D_] + [
+            _c_int64_p, I64, _c_double_p, _c_double_p]
+        lib.oracle_attn_bwd_ex.restype = I
+        lib.oracle_attn_bwd_ex.argtypes = [_c_double_p] * 7 + [I64] * 5 + [I, I64, I64, D_]
+        lib.oracle_attn_bwd_rows_ex.restype = I
+        lib.oracle_attn_bwd_rows_ex.argtypes = [_c_double_p] * 4 + [I64] * 5 + [I, I64, I64, D_] + [
+            _c_int64_p, I64, _c_double_p, _c_int64_p, I64, _c_double_p, _c_double_p]
+        lib.oracle_num_threads.restype = I
         lib.oracle_num_threads.argtypes = []
         self._lib = lib
         self.path = library
@@ -82,73 +106,69 @@ class Oracle:
     def num_threads(self) -> int:
         return int(self._lib.oracle_num_threads())
 
-    def attention(self, q, k, v, causal: bool, scale: float):
-        """Exact attention over all rows.  q, k, v: [B,H,S,D]; returns (o [B,H,S,D], lse [B,H,S])."""
+    def attention(self, q, k, v, causal: bool, scale: float, window=None):
+        """Exact attention over all rows: returns (o [B,H,S,D], lse [B,H,S])."""
         q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
-        if q.ndim != 4 or k.shape != q.shape or v.shape != q.shape:
-            raise ValueError(f"q, k, v must share one [B,H,S,D] shape, got {q.shape}, {k.shape}, {v.shape}")
-        B, H, S, D = q.shape
+        B, H, Hkv, S, D = _shapes(q, k, v)
+        wl, wr = _window(window)
         o = np.empty_like(q)
         lse = np.empty((B, H, S), dtype=np.float64)
-        rc = self._lib.oracle_attn_fwd(self._ptr(q), self._ptr(k), self._ptr(v), self._ptr(o),
-                                       self._ptr(lse), B, H, S, D, int(bool(causal)), float(scale))
+        rc = self._lib.oracle_attn_fwd_ex(self._ptr(q), self._ptr(k), self._ptr(v), self._ptr(o),
+                                          self._ptr(lse), B, H, Hkv, S, D, int(bool(causal)), wl, wr,
+                                          float(scale))
         if rc != 0:
-            raise ValueError(f"oracle_attn_fwd failed with status {rc}")
+            raise ValueError(f"oracle_attn_fwd_ex failed with status {rc}")
         return o, lse
 
-    def attention_rows(self, q, k, v, causal: bool, scale: float, rows):
-        """Exact attention for selected flat rows ``(b*H + h)*S + i``.
-
-        Returns (o [n, D], lse [n]) in the order of ``rows``.
-        """
+    def attention_rows(self, q, k, v, causal: bool, scale: float, rows, window=None):
+        """Exact attention for selected flat query rows ``(b*H + h)*S + i``:
+        returns (o [n, D], lse [n]) in the order of ``rows``."""
         q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
-        if q.ndim != 4 or k.shape != q.shape or v.shape != q.shape:
-            raise ValueError("q, k, v must share one [B,H,S,D] shape")
-        B, H, S, D = q.shape
+        B, H, Hkv, S, D = _shapes(q, k, v)
+        wl, wr = _window(window)
         rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
         n = rows.shape[0]
         o = np.empty((n, D), dtype=np.float64)
         lse = np.empty((n,), dtype=np.float64)
-        rc = self._lib.oracle_attn_fwd_rows(
-            self._ptr(q), self._ptr(k), self._ptr(v), B, H, S, D, int(bool(causal)), float(scale),
-            rows.ctypes.data_as(_c_int64_p), n, self._ptr(o), self._ptr(lse))
+        rc = self._lib.oracle_attn_fwd_rows_ex(
+            self._ptr(q), self._ptr(k), self._ptr(v), B, H, Hkv, S, D, int(bool(causal)), wl, wr,
+            float(scale), rows.ctypes.data_as(_c_int64_p), n, self._ptr(o), self._ptr(lse))
         if rc != 0:
-            raise ValueError(f"oracle_attn_fwd_rows failed with status {rc}")
+            raise ValueError(f"oracle_attn_fwd_rows_ex failed with status {rc}")
         return o, lse
 
-    def attention_bwd(self, q, k, v, dout, causal: bool, scale: float):
-        """Gradients of exact attention for upstream gradient ``dout``.
-
-        q, k, v, dout: [B,H,S,D]; returns (dq, dk, dv), each [B,H,S,D].
-        """
+    def attention_bwd(self, q, k, v, dout, causal: bool, scale: float, window=None):
+        """Gradients for upstream gradient ``dout`` [B,H,S,D]: returns
+        (dq [B,H,S,D], dk [B,Hkv,S,D], dv [B,Hkv,S,D])."""
         q, k, v, dout = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(dout)
-        if q.ndim != 4 or any(x.shape != q.shape for x in (k, v, dout)):
-            raise ValueError("q, k, v, dout must share one [B,H,S,D] shape")
-        B, H, S, D = q.shape
-        dq, dk, dv = np.empty_like(q), np.empty_like(q), np.empty_like(q)
-        rc = self._lib.oracle_attn_bwd(self._ptr(q), self._ptr(k), self._ptr(v), self._ptr(dout),
-                                       self._ptr(dq), self._ptr(dk), self._ptr(dv),
-                                       B, H, S, D, int(bool(causal)), float(scale))
+        B, H, Hkv, S, D = _shapes(q, k, v, (dout,))
+        wl, wr = _window(window)
+        dq, dk, dv = np.empty_like(q), np.empty_like(k), np.empty_like(k)
+        rc = self._lib.oracle_attn_bwd_ex(self._ptr(q), self._ptr(k), self._ptr(v), self._ptr(dout),
+                                          self._ptr(dq), self._ptr(dk), self._ptr(dv),
+                                          B, H, Hkv, S, D, int(bool(causal)), wl, wr, float(scale))
         if rc != 0:
-            raise ValueError(f"oracle_attn_bwd failed with status {rc}")
+            raise ValueError(f"oracle_attn_bwd_ex failed with status {rc}")
         return dq, dk, dv
 
-    def attention_bwd_rows(self, q, k, v, dout, causal: bool, scale: float, rows):
-        """Gradients at selected flat positions ``(b*H + h)*S + t``: dQ of query t
-        and dK, dV of key t.  Returns (dq [n,D], dk [n,D], dv [n,D])."""
+    def attention_bwd_rows(self, q, k, v, dout, causal: bool, scale: float, rows, krows=None, window=None):
+        """Gradients at selected positions: dQ of flat query rows ``rows``
+        ((b*H + h)*S + t) and dK, dV of flat key rows ``krows`` ((b*Hkv + hk)*S + t;
+        default: the same indices as ``rows``).  Returns (dq [n,D], dk [m,D], dv [m,D])."""
         q, k, v, dout = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(dout)
-        if q.ndim != 4 or any(x.shape != q.shape for x in (k, v, dout)):
-            raise ValueError("q, k, v, dout must share one [B,H,S,D] shape")
-        B, H, S, D = q.shape
+        B, H, Hkv, S, D = _shapes(q, k, v, (dout,))
+        wl, wr = _window(window)
         rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
-        n = rows.shape[0]
-        dq, dk, dv = (np.empty((n, D), dtype=np.float64) for _ in range(3))
-        rc = self._lib.oracle_attn_bwd_rows(
-            self._ptr(q), self._ptr(k), self._ptr(v), self._ptr(dout), B, H, S, D,
-            int(bool(causal)), float(scale), rows.ctypes.data_as(_c_int64_p), n,
-            self._ptr(dq), self._ptr(dk), self._ptr(dv))
+        krows = rows if krows is None else np.ascontiguousarray(np.asarray(krows, dtype=np.int64))
+        n, m = rows.shape[0], krows.shape[0]
+        dq = np.empty((n, D), dtype=np.float64)
+        dk, dv = np.empty((m, D), dtype=np.float64), np.empty((m, D), dtype=np.float64)
+        rc = self._lib.oracle_attn_bwd_rows_ex(
+            self._ptr(q), self._ptr(k), self._ptr(v), self._ptr(dout), B, H, Hkv, S, D,
+            int(bool(causal)), wl, wr, float(scale), rows.ctypes.data_as(_c_int64_p), n, self._ptr(dq),
+            krows.ctypes.data_as(_c_int64_p), m, self._ptr(dk), self._ptr(dv))
         if rc != 0:
-            raise ValueError(f"oracle_attn_bwd_rows failed with status {rc}")
+            raise ValueError(f"oracle_attn_bwd_rows_ex failed with status {rc}")
         return dq, dk, dv
 
 
@@ -167,17 +187,17 @@ def default() -> Oracle:
     return _DEFAULT
 
 
-def attention(q, k, v, causal: bool, scale: float):
-    return default().attention(q, k, v, causal, scale)
+def attention(q, k, v, causal: bool, scale: float, window=None):
+    return default().attention(q, k, v, causal, scale, window)
 
 
-def attention_rows(q, k, v, causal: bool, scale: float, rows):
-    return default().attention_rows(q, k, v, causal, scale, rows)
+def attention_rows(q, k, v, causal: bool, scale: float, rows, window=None):
+    return default().attention_rows(q, k, v, causal, scale, rows, window)
 
 
-def attention_bwd(q, k, v, dout, causal: bool, scale: float):
-    return default().attention_bwd(q, k, v, dout, causal, scale)
+def attention_bwd(q, k, v, dout, causal: bool, scale: float, window=None):
+    return default().attention_bwd(q, k, v, dout, causal, scale, window)
 
 
-def attention_bwd_rows(q, k, v, dout, causal: bool, scale: float, rows):
-    return default().attention_bwd_rows(q, k, v, dout, causal, scale, rows)
+def attention_bwd_rows(q, k, v, dout, causal: bool, scale: float, rows, krows=None, window=None):
+    return default().attention_bwd_rows(q, k, v, dout, causal, scale, rows, krows, window)

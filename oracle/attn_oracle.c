@@ -12,7 +12,9 @@
  * the backward, further down, is described where it is defined):
  *
  *   For every batch b, head h and query row i, with the attended key set
- *   J = {0..S-1} (non-causal) or J = {0..i} (causal, key j visible iff j <= i):
+ *   J = {0..S-1} (non-causal) or J = {0..i} (causal, key j visible iff j <= i),
+ *   narrowed to i - left .. i + right by an optional window (see key_range),
+ *   and keys / values taken from the head's key/value head (see kv_head):
  *
  *     s_j    = scale * sum_{d=0}^{D-1} q[i,d] * k[j,d]          (j in J)
  *     m      = max_{j in J} s_j
@@ -100,11 +102,16 @@ static void attend_one_row(const double *q_i, const double *k_bh, const double *
 }
 
 static int check_args(const double *q, const double *k, const double *v,
-                      int64_t B, int64_t H, int64_t S, int64_t D, int causal)
+                      int64_t B, int64_t H, int64_t Hkv, int64_t S, int64_t D, int causal,
+                      int64_t wl, int64_t wr)
 {
     if (B < 0 || H < 0 || S < 0 || D <= 0)
         return ORACLE_BAD_ARGS;
+    if (Hkv <= 0 ? H != 0 : H % Hkv != 0)
+        return ORACLE_BAD_ARGS;
     if (causal != 0 && causal != 1)
+        return ORACLE_BAD_ARGS;
+    if (wl < -1 || wr < -1)
         return ORACLE_BAD_ARGS;
     if (B * H * S > 0 && (!q || !k || !v))
         return ORACLE_BAD_ARGS;
@@ -112,15 +119,47 @@ static int check_args(const double *q, const double *k, const double *v,
 }
 
 /*
+ * The keys query i attends to form one range [*lo, *hi]: 0 .. S-1, cut at i
+ * by causal masking (key j visible iff j <= i), at i - wl by a left window
+ * and at i + wr by a right window (wl, wr = -1: no limit on that side).
+ * This is the window_size = (left, right) convention of "Inside
+ * FlashAttention", section 6.1; for square attention the range always holds
+ * key i itself.
+ */
+static void key_range(int64_t i, int64_t S, int causal, int64_t wl, int64_t wr,
+                      int64_t *lo, int64_t *hi)
+{
+    int64_t a = 0, b = causal ? i : S - 1;
+    if (wl >= 0 && i - wl > a)
+        a = i - wl;
+    if (wr >= 0 && i + wr < b)
+        b = i + wr;
+    *lo = a;
+    *hi = b;
+}
+
+/*
+ * Grouped heads (GQA / MQA, "Inside FlashAttention", section 6.1): H query
+ * heads share Hkv key/value heads, G = H / Hkv consecutive query heads per
+ * key/value head, so query head bh = b*H + h reads key/value head
+ * b*Hkv + h / G = bh / G.
+ */
+static int64_t kv_head(int64_t bh, int64_t H, int64_t Hkv)
+{
+    return bh / (H / Hkv);
+}
+
+/*
  * Attention over selected rows.  rows[r] is a flat row index
  * (b*H + h)*S + i; the row's output goes to o_rows[r*D .. r*D+D-1] and
  * lse_rows[r].  Returns ORACLE_OK, or an error code without writing anything.
  */
-int oracle_attn_fwd_rows(const double *q, const double *k, const double *v,
-                         int64_t B, int64_t H, int64_t S, int64_t D, int causal, double scale,
-                         const int64_t *rows, int64_t n_rows, double *o_rows, double *lse_rows)
+int oracle_attn_fwd_rows_ex(const double *q, const double *k, const double *v,
+                            int64_t B, int64_t H, int64_t Hkv, int64_t S, int64_t D, int causal,
+                            int64_t wl, int64_t wr, double scale,
+                            const int64_t *rows, int64_t n_rows, double *o_rows, double *lse_rows)
 {
-    int rc = check_args(q, k, v, B, H, S, D, causal);
+    int rc = check_args(q, k, v, B, H, Hkv, S, D, causal, wl, wr);
     if (rc != ORACLE_OK)
         return rc;
     if (n_rows < 0 || (n_rows > 0 && (!rows || !o_rows || !lse_rows)))
@@ -146,10 +185,12 @@ int oracle_attn_fwd_rows(const double *q, const double *k, const double *v,
             const int64_t flat = rows[r];
             const int64_t bh = flat / S;
             const int64_t i = flat % S;
-            const double *k_bh = k + bh * S * D;
-            const double *v_bh = v + bh * S * D;
-            const int64_t n_keys = causal ? i + 1 : S;
-            attend_one_row(q + flat * D, k_bh, v_bh, n_keys, D, scale, p, acc,
+            const int64_t kvh = kv_head(bh, H, Hkv);
+            const double *k_bh = k + kvh * S * D;
+            const double *v_bh = v + kvh * S * D;
+            int64_t lo, hi;
+            key_range(i, S, causal, wl, wr, &lo, &hi);
+            attend_one_row(q + flat * D, k_bh + lo * D, v_bh + lo * D, hi - lo + 1, D, scale, p, acc,
                            o_rows + r * D, lse_rows + r);
         }
         free(p);
@@ -158,11 +199,12 @@ int oracle_attn_fwd_rows(const double *q, const double *k, const double *v,
     return failed ? ORACLE_NO_MEMORY : ORACLE_OK;
 }
 
-/* Attention over every row: o is [B,H,S,D], lse is [B,H,S]. */
-int oracle_attn_fwd(const double *q, const double *k, const double *v, double *o, double *lse,
-                    int64_t B, int64_t H, int64_t S, int64_t D, int causal, double scale)
+/* Attention over every row: o is [B,H,S,D], lse is [B,H,S]; k, v are [B,Hkv,S,D]. */
+int oracle_attn_fwd_ex(const double *q, const double *k, const double *v, double *o, double *lse,
+                       int64_t B, int64_t H, int64_t Hkv, int64_t S, int64_t D, int causal,
+                       int64_t wl, int64_t wr, double scale)
 {
-    int rc = check_args(q, k, v, B, H, S, D, causal);
+    int rc = check_args(q, k, v, B, H, Hkv, S, D, causal, wl, wr);
     if (rc != ORACLE_OK)
         return rc;
     const int64_t total = B * H * S;
@@ -186,14 +228,30 @@ int oracle_attn_fwd(const double *q, const double *k, const double *v, double *o
                 continue;
             const int64_t bh = flat / S;
             const int64_t i = flat % S;
-            const int64_t n_keys = causal ? i + 1 : S;
-            attend_one_row(q + flat * D, k + bh * S * D, v + bh * S * D, n_keys, D, scale,
-                           p, acc, o + flat * D, lse + flat);
+            const int64_t kvh = kv_head(bh, H, Hkv);
+            int64_t lo, hi;
+            key_range(i, S, causal, wl, wr, &lo, &hi);
+            attend_one_row(q + flat * D, k + (kvh * S + lo) * D, v + (kvh * S + lo) * D, hi - lo + 1, D,
+                           scale, p, acc, o + flat * D, lse + flat);
         }
         free(p);
         free(acc);
     }
     return failed ? ORACLE_NO_MEMORY : ORACLE_OK;
+}
+
+int oracle_attn_fwd_rows(const double *q, const double *k, const double *v,
+                         int64_t B, int64_t H, int64_t S, int64_t D, int causal, double scale,
+                         const int64_t *rows, int64_t n_rows, double *o_rows, double *lse_rows)
+{
+    return oracle_attn_fwd_rows_ex(q, k, v, B, H, H, S, D, causal, -1, -1, scale, rows, n_rows, o_rows,
+                                   lse_rows);
+}
+
+int oracle_attn_fwd(const double *q, const double *k, const double *v, double *o, double *lse,
+                    int64_t B, int64_t H, int64_t S, int64_t D, int causal, double scale)
+{
+    return oracle_attn_fwd_ex(q, k, v, o, lse, B, H, H, S, D, causal, -1, -1, scale);
 }
 
 /* ------------------------------------------------------------------------
@@ -208,6 +266,9 @@ int oracle_attn_fwd(const double *q, const double *k, const double *v, double *o
  *   dQ_i  = scale * sum_j dS_ij K_j
  *   dK_j  = scale * sum_i dS_ij Q_i
  *
+ * With grouped heads, a key/value head's dK and dV sum these terms over the
+ * query heads that share it.
+ *
  * Sources: "从零训练语言模型（第二部分）", section "反向传播" (the same five
  * equations, the row term there being rowsum(dO o O), which equals
  * sum_t P_it dP_it because O_i = sum_t P_it V_t); the CS336 write-up's
@@ -217,7 +278,7 @@ int oracle_attn_fwd(const double *q, const double *k, const double *v, double *o
  * from P and dP, not from O.
  * ------------------------------------------------------------------------ */
 
-/* Softmax weights of one query row over keys 0..n_keys-1: w[j] = P_ij. */
+/* Softmax weights of one query row over n_keys keys: w[j] = P_ij. */
 static void bwd_row_weights(const double *q_i, const double *k_bh, int64_t n_keys, int64_t D,
                             double scale, double *w)
 {
@@ -240,7 +301,7 @@ static void bwd_row_weights(const double *q_i, const double *k_bh, int64_t n_key
         w[j] /= total;
 }
 
-/* g[j] = dP_ij = <dO_i, V_j> for keys 0..n_keys-1; returns sum_j P_ij dP_ij. */
+/* g[j] = dP_ij = <dO_i, V_j> over n_keys keys; returns sum_j P_ij dP_ij. */
 static double bwd_row_dp(const double *do_i, const double *v_bh, int64_t n_keys, int64_t D,
                          const double *w, double *g)
 {
@@ -256,51 +317,60 @@ static double bwd_row_dp(const double *do_i, const double *v_bh, int64_t n_keys,
     return row;
 }
 
-/* Gradients of one head: dq, dk, dv are [S,D] and fully written. */
-static void bwd_one_head(const double *q_bh, const double *k_bh, const double *v_bh, const double *do_bh,
-                         int64_t S, int64_t D, int causal, double scale,
-                         double *dq_bh, double *dk_bh, double *dv_bh, double *w, double *g)
+/*
+ * Gradients for one key/value head and the G query heads that read it:
+ * q_g, do_g, dq_g are those G heads' [G,S,D] blocks; k_h, v_h, dk_h, dv_h the
+ * key/value head's [S,D].  Everything is written.
+ */
+static void bwd_one_group(const double *q_g, const double *k_h, const double *v_h, const double *do_g,
+                          int64_t G, int64_t S, int64_t D, int causal, int64_t wl, int64_t wr, double scale,
+                          double *dq_g, double *dk_h, double *dv_h, double *w, double *g)
 {
     for (int64_t x = 0; x < S * D; ++x) {
-        dk_bh[x] = 0.0;
-        dv_bh[x] = 0.0;
+        dk_h[x] = 0.0;
+        dv_h[x] = 0.0;
     }
-    for (int64_t i = 0; i < S; ++i) {
-        const int64_t n_keys = causal ? i + 1 : S;
-        const double *q_i = q_bh + i * D;
-        const double *do_i = do_bh + i * D;
-        bwd_row_weights(q_i, k_bh, n_keys, D, scale, w);
-        const double row = bwd_row_dp(do_i, v_bh, n_keys, D, w, g);
-        double *dq_i = dq_bh + i * D;
-        for (int64_t d = 0; d < D; ++d)
-            dq_i[d] = 0.0;
-        for (int64_t j = 0; j < n_keys; ++j) {
-            const double ds = w[j] * (g[j] - row);
-            const double *kr = k_bh + j * D;
-            double *dk_j = dk_bh + j * D;
-            double *dv_j = dv_bh + j * D;
-            for (int64_t d = 0; d < D; ++d) {
-                dq_i[d] += scale * ds * kr[d];
-                dk_j[d] += scale * ds * q_i[d];
-                dv_j[d] += w[j] * do_i[d];
+    for (int64_t hq = 0; hq < G; ++hq) {
+        for (int64_t i = 0; i < S; ++i) {
+            int64_t lo, hi;
+            key_range(i, S, causal, wl, wr, &lo, &hi);
+            const int64_t n_keys = hi - lo + 1;
+            const double *q_i = q_g + (hq * S + i) * D;
+            const double *do_i = do_g + (hq * S + i) * D;
+            bwd_row_weights(q_i, k_h + lo * D, n_keys, D, scale, w);
+            const double row = bwd_row_dp(do_i, v_h + lo * D, n_keys, D, w, g);
+            double *dq_i = dq_g + (hq * S + i) * D;
+            for (int64_t d = 0; d < D; ++d)
+                dq_i[d] = 0.0;
+            for (int64_t j = 0; j < n_keys; ++j) {
+                const double ds = w[j] * (g[j] - row);
+                const double *kr = k_h + (lo + j) * D;
+                double *dk_j = dk_h + (lo + j) * D;
+                double *dv_j = dv_h + (lo + j) * D;
+                for (int64_t d = 0; d < D; ++d) {
+                    dq_i[d] += scale * ds * kr[d];
+                    dk_j[d] += scale * ds * q_i[d];
+                    dv_j[d] += w[j] * do_i[d];
+                }
             }
         }
     }
 }
 
-/* Gradients of every head: dq, dk, dv are [B,H,S,D]. */
-int oracle_attn_bwd(const double *q, const double *k, const double *v, const double *dout,
-                    double *dq, double *dk, double *dv,
-                    int64_t B, int64_t H, int64_t S, int64_t D, int causal, double scale)
+/* Gradients: dq is [B,H,S,D], dk and dv are [B,Hkv,S,D]. */
+int oracle_attn_bwd_ex(const double *q, const double *k, const double *v, const double *dout,
+                       double *dq, double *dk, double *dv,
+                       int64_t B, int64_t H, int64_t Hkv, int64_t S, int64_t D, int causal,
+                       int64_t wl, int64_t wr, double scale)
 {
-    int rc = check_args(q, k, v, B, H, S, D, causal);
+    int rc = check_args(q, k, v, B, H, Hkv, S, D, causal, wl, wr);
     if (rc != ORACLE_OK)
         return rc;
     if (B * H * S == 0)
         return ORACLE_OK;
     if (!dout || !dq || !dk || !dv)
         return ORACLE_BAD_ARGS;
-    const int64_t heads = B * H;
+    const int64_t groups = B * Hkv, G = H / Hkv;
     int failed = 0;
 #pragma omp parallel
     {
@@ -311,12 +381,12 @@ int oracle_attn_bwd(const double *q, const double *k, const double *v, const dou
             failed = 1;
         }
 #pragma omp for schedule(dynamic, 1)
-        for (int64_t bh = 0; bh < heads; ++bh) {
+        for (int64_t kvh = 0; kvh < groups; ++kvh) {
             if (!w || !g)
                 continue;
-            const int64_t base = bh * S * D;
-            bwd_one_head(q + base, k + base, v + base, dout + base, S, D, causal, scale,
-                         dq + base, dk + base, dv + base, w, g);
+            const int64_t qbase = kvh * G * S * D, kbase = kvh * S * D;
+            bwd_one_group(q + qbase, k + kbase, v + kbase, dout + qbase, G, S, D, causal, wl, wr, scale,
+                          dq + qbase, dk + kbase, dv + kbase, w, g);
         }
         free(w);
         free(g);
@@ -324,143 +394,189 @@ int oracle_attn_bwd(const double *q, const double *k, const double *v, const dou
     return failed ? ORACLE_NO_MEMORY : ORACLE_OK;
 }
 
-/*
- * Gradients at selected positions.  rows[r] is a flat index (b*H + h)*S + t;
- * dq_rows[r*D ..] receives dQ of query t, dk_rows / dv_rows of key t (all of
- * head b*H + h).  Every head named by `rows` first gets, for all of its query
- * rows i, the softmax maximum and sum and the row term sum_j P_ij dP_ij; then
- * each key gradient is one pass over the queries that see the key.
- */
-int oracle_attn_bwd_rows(const double *q, const double *k, const double *v, const double *dout,
-                         int64_t B, int64_t H, int64_t S, int64_t D, int causal, double scale,
-                         const int64_t *rows, int64_t n_rows,
-                         double *dq_rows, double *dk_rows, double *dv_rows)
+int oracle_attn_bwd(const double *q, const double *k, const double *v, const double *dout,
+                    double *dq, double *dk, double *dv,
+                    int64_t B, int64_t H, int64_t S, int64_t D, int causal, double scale)
 {
-    int rc = check_args(q, k, v, B, H, S, D, causal);
+    return oracle_attn_bwd_ex(q, k, v, dout, dq, dk, dv, B, H, H, S, D, causal, -1, -1, scale);
+}
+
+/*
+ * Gradients at selected positions.  qrows[r] is a flat query-row index
+ * (b*H + h)*S + t: dq_rows[r*D ..] receives dQ of that row.  krows[r] is a
+ * flat key/value-row index (b*Hkv + hk)*S + t: dk_rows / dv_rows[r*D ..]
+ * receive dK and dV of that key, summed over the query heads of its group.
+ * Every key/value head named by `krows` first gets, for all query rows of its
+ * group, the softmax maximum and sum and the row term sum_j P_ij dP_ij; then
+ * each key gradient is one pass over the rows that see the key.
+ */
+int oracle_attn_bwd_rows_ex(const double *q, const double *k, const double *v, const double *dout,
+                            int64_t B, int64_t H, int64_t Hkv, int64_t S, int64_t D, int causal,
+                            int64_t wl, int64_t wr, double scale,
+                            const int64_t *qrows, int64_t n_qrows, double *dq_rows,
+                            const int64_t *krows, int64_t n_krows, double *dk_rows, double *dv_rows)
+{
+    int rc = check_args(q, k, v, B, H, Hkv, S, D, causal, wl, wr);
     if (rc != ORACLE_OK)
         return rc;
-    if (n_rows < 0 || (n_rows > 0 && (!rows || !dout || !dq_rows || !dk_rows || !dv_rows)))
+    if (n_qrows < 0 || n_krows < 0 || (n_qrows > 0 && (!qrows || !dout || !dq_rows)) ||
+        (n_krows > 0 && (!krows || !dout || !dk_rows || !dv_rows)))
         return ORACLE_BAD_ARGS;
-    const int64_t total = B * H * S;
-    for (int64_t r = 0; r < n_rows; ++r)
-        if (rows[r] < 0 || rows[r] >= total)
+    for (int64_t r = 0; r < n_qrows; ++r)
+        if (qrows[r] < 0 || qrows[r] >= B * H * S)
             return ORACLE_BAD_ARGS;
-    if (n_rows == 0)
+    for (int64_t r = 0; r < n_krows; ++r)
+        if (krows[r] < 0 || krows[r] >= B * Hkv * S)
+            return ORACLE_BAD_ARGS;
+    if (n_qrows + n_krows == 0)
         return ORACLE_OK;
 
-    /* heads that are needed, and their per-row statistics */
-    const int64_t heads = B * H;
-    int64_t *slot = (int64_t *)malloc((size_t)heads * sizeof(int64_t));
+    /* key/value heads that are needed, and the statistics of their groups' rows */
+    const int64_t G = H / Hkv, kvheads = B * Hkv;
+    int64_t *slot = (int64_t *)malloc((size_t)(kvheads > 0 ? kvheads : 1) * sizeof(int64_t));
     if (!slot)
         return ORACLE_NO_MEMORY;
-    for (int64_t bh = 0; bh < heads; ++bh)
-        slot[bh] = -1;
-    int64_t n_heads = 0;
-    for (int64_t r = 0; r < n_rows; ++r) {
-        const int64_t bh = rows[r] / S;
-        if (slot[bh] < 0)
-            slot[bh] = n_heads++;
+    for (int64_t x = 0; x < kvheads; ++x)
+        slot[x] = -1;
+    int64_t n_groups = 0;
+    for (int64_t r = 0; r < n_krows; ++r) {
+        const int64_t kvh = krows[r] / S;
+        if (slot[kvh] < 0)
+            slot[kvh] = n_groups++;
     }
-    int64_t *head_of = (int64_t *)malloc((size_t)n_heads * sizeof(int64_t));
-    double *top = (double *)malloc((size_t)(n_heads * S) * sizeof(double));
-    double *sum = (double *)malloc((size_t)(n_heads * S) * sizeof(double));
-    double *rowt = (double *)malloc((size_t)(n_heads * S) * sizeof(double));
-    if (!head_of || !top || !sum || !rowt) {
-        free(slot); free(head_of); free(top); free(sum); free(rowt);
+    const int64_t n_stat = n_groups * G * S;
+    int64_t *group_of = (int64_t *)malloc((size_t)(n_groups > 0 ? n_groups : 1) * sizeof(int64_t));
+    double *top = (double *)malloc((size_t)(n_stat > 0 ? n_stat : 1) * sizeof(double));
+    double *sum = (double *)malloc((size_t)(n_stat > 0 ? n_stat : 1) * sizeof(double));
+    double *rowt = (double *)malloc((size_t)(n_stat > 0 ? n_stat : 1) * sizeof(double));
+    if (!group_of || !top || !sum || !rowt) {
+        free(slot); free(group_of); free(top); free(sum); free(rowt);
         return ORACLE_NO_MEMORY;
     }
-    for (int64_t bh = 0; bh < heads; ++bh)
-        if (slot[bh] >= 0)
-            head_of[slot[bh]] = bh;
+    for (int64_t x = 0; x < kvheads; ++x)
+        if (slot[x] >= 0)
+            group_of[slot[x]] = x;
 
     int failed = 0;
 #pragma omp parallel
     {
-        double *w = (double *)malloc((size_t)S * sizeof(double));
-        double *g = (double *)malloc((size_t)S * sizeof(double));
+        double *w = (double *)malloc((size_t)(S > 0 ? S : 1) * sizeof(double));
+        double *g = (double *)malloc((size_t)(S > 0 ? S : 1) * sizeof(double));
         if (!w || !g) {
 #pragma omp atomic write
             failed = 1;
         }
-        /* per query row i of each needed head: max, sum and row term */
+        /* per query row of each needed group: max, sum and row term */
 #pragma omp for schedule(dynamic, 16)
-        for (int64_t x = 0; x < n_heads * S; ++x) {
+        for (int64_t x = 0; x < n_stat; ++x) {
             if (!w || !g)
                 continue;
-            const int64_t hs = x / S, i = x % S;
-            const int64_t base = head_of[hs] * S * D;
-            const int64_t n_keys = causal ? i + 1 : S;
-            const double *q_i = q + base + i * D;
-            double hi = -INFINITY;
+            const int64_t gs = x / (G * S), hq = (x / S) % G, i = x % S;
+            const int64_t kvh = group_of[gs];
+            const int64_t qrow = (kvh * G + hq) * S + i;
+            const double *q_i = q + qrow * D;
+            const double *k_h = k + kvh * S * D, *v_h = v + kvh * S * D;
+            int64_t lo, hi;
+            key_range(i, S, causal, wl, wr, &lo, &hi);
+            const int64_t n_keys = hi - lo + 1;
+            double mx = -INFINITY;
             for (int64_t j = 0; j < n_keys; ++j) {
-                const double *kr = k + base + j * D;
+                const double *kr = k_h + (lo + j) * D;
                 double acc = 0.0;
                 for (int64_t d = 0; d < D; ++d)
                     acc += q_i[d] * kr[d];
                 w[j] = scale * acc;
-                if (w[j] > hi)
-                    hi = w[j];
+                if (w[j] > mx)
+                    mx = w[j];
             }
             double l = 0.0;
             for (int64_t j = 0; j < n_keys; ++j) {
-                w[j] = exp(w[j] - hi);
+                w[j] = exp(w[j] - mx);
                 l += w[j];
             }
             for (int64_t j = 0; j < n_keys; ++j)
                 w[j] /= l;
-            top[x] = hi;
+            top[x] = mx;
             sum[x] = l;
-            rowt[x] = bwd_row_dp(dout + base + i * D, v + base, n_keys, D, w, g);
+            rowt[x] = bwd_row_dp(dout + qrow * D, v_h + lo * D, n_keys, D, w, g);
         }
-        /* each requested position: dQ of its query, dK and dV of its key */
+        /* dQ of each requested query row */
 #pragma omp for schedule(dynamic, 1)
-        for (int64_t r = 0; r < n_rows; ++r) {
+        for (int64_t r = 0; r < n_qrows; ++r) {
             if (!w || !g)
                 continue;
-            const int64_t bh = rows[r] / S, t = rows[r] % S;
-            const int64_t hs = slot[bh];
-            const int64_t base = bh * S * D;
-            const int64_t n_keys = causal ? t + 1 : S;
-            bwd_row_weights(q + base + t * D, k + base, n_keys, D, scale, w);
-            const double row = bwd_row_dp(dout + base + t * D, v + base, n_keys, D, w, g);
+            const int64_t bh = qrows[r] / S, t = qrows[r] % S;
+            const int64_t kvh = kv_head(bh, H, Hkv);
+            const double *k_h = k + kvh * S * D, *v_h = v + kvh * S * D;
+            int64_t lo, hi;
+            key_range(t, S, causal, wl, wr, &lo, &hi);
+            const int64_t n_keys = hi - lo + 1;
+            bwd_row_weights(q + qrows[r] * D, k_h + lo * D, n_keys, D, scale, w);
+            const double row = bwd_row_dp(dout + qrows[r] * D, v_h + lo * D, n_keys, D, w, g);
             double *dq_t = dq_rows + r * D;
-            double *dk_t = dk_rows + r * D;
-            double *dv_t = dv_rows + r * D;
-            for (int64_t d = 0; d < D; ++d) {
+            for (int64_t d = 0; d < D; ++d)
                 dq_t[d] = 0.0;
-                dk_t[d] = 0.0;
-                dv_t[d] = 0.0;
-            }
             for (int64_t j = 0; j < n_keys; ++j) {
                 const double ds = w[j] * (g[j] - row);
                 for (int64_t d = 0; d < D; ++d)
-                    dq_t[d] += scale * ds * k[base + j * D + d];
+                    dq_t[d] += scale * ds * k_h[(lo + j) * D + d];
             }
-            /* key t is seen by queries i >= t (causal) or by all */
-            const double *k_t = k + base + t * D;
-            const double *v_t = v + base + t * D;
-            for (int64_t i = causal ? t : 0; i < S; ++i) {
-                const double *q_i = q + base + i * D;
-                const double *do_i = dout + base + i * D;
-                double acc = 0.0, dpv = 0.0;
-                for (int64_t d = 0; d < D; ++d) {
-                    acc += q_i[d] * k_t[d];
-                    dpv += do_i[d] * v_t[d];
-                }
-                const int64_t x = hs * S + i;
-                const double p = exp(scale * acc - top[x]) / sum[x];
-                const double ds = p * (dpv - rowt[x]);
-                for (int64_t d = 0; d < D; ++d) {
-                    dk_t[d] += scale * ds * q_i[d];
-                    dv_t[d] += p * do_i[d];
+        }
+        /* dK and dV of each requested key: every row of the group that sees it */
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t r = 0; r < n_krows; ++r) {
+            const int64_t kvh = krows[r] / S, t = krows[r] % S;
+            const int64_t gs = slot[kvh];
+            const double *k_t = k + krows[r] * D;
+            const double *v_t = v + krows[r] * D;
+            double *dk_t = dk_rows + r * D;
+            double *dv_t = dv_rows + r * D;
+            for (int64_t d = 0; d < D; ++d) {
+                dk_t[d] = 0.0;
+                dv_t[d] = 0.0;
+            }
+            for (int64_t hq = 0; hq < G; ++hq) {
+                for (int64_t i = 0; i < S; ++i) {
+                    int64_t lo, hi;
+                    key_range(i, S, causal, wl, wr, &lo, &hi);
+                    if (t < lo || t > hi)
+                        continue;
+                    const int64_t qrow = (kvh * G + hq) * S + i;
+                    const double *q_i = q + qrow * D;
+                    const double *do_i = dout + qrow * D;
+                    double acc = 0.0, dpv = 0.0;
+                    for (int64_t d = 0; d < D; ++d) {
+                        acc += q_i[d] * k_t[d];
+                        dpv += do_i[d] * v_t[d];
+                    }
+                    const int64_t x = (gs * G + hq) * S + i;
+                    const double p = exp(scale * acc - top[x]) / sum[x];
+                    const double ds = p * (dpv - rowt[x]);
+                    for (int64_t d = 0; d < D; ++d) {
+                        dk_t[d] += scale * ds * q_i[d];
+                        dv_t[d] += p * do_i[d];
+                    }
                 }
             }
         }
         free(w);
         free(g);
     }
-    free(slot); free(head_of); free(top); free(sum); free(rowt);
+    free(slot); free(group_of); free(top); free(sum); free(rowt);
     return failed ? ORACLE_NO_MEMORY : ORACLE_OK;
+}
+
+/*
+ * Gradients at selected positions (one head per key/value head): for rows[r] =
+ * (b*H + h)*S + t, dQ of query t and dK, dV of key t of that head.
+ */
+int oracle_attn_bwd_rows(const double *q, const double *k, const double *v, const double *dout,
+                         int64_t B, int64_t H, int64_t S, int64_t D, int causal, double scale,
+                         const int64_t *rows, int64_t n_rows,
+                         double *dq_rows, double *dk_rows, double *dv_rows)
+{
+    return oracle_attn_bwd_rows_ex(q, k, v, dout, B, H, H, S, D, causal, -1, -1, scale, rows, n_rows, dq_rows,
+                                   rows, n_rows, dk_rows, dv_rows);
 }
 
 /* Number of OpenMP threads a parallel region of the oracle uses. */

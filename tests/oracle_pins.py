@@ -398,6 +398,143 @@ def pin_bwd_rows_entry(orc):
         _close(rk, dk.reshape(-1, D)[rows], 1e-13, "rows entry dK")
         _close(rv, dv.reshape(-1, D)[rows], 1e-13, "rows entry dV")
 
+
+# ------------------------------------------- grouped heads and sliding windows
+# Grouped heads (GQA / MQA) and window_size = (left, right) ("Inside
+# FlashAttention", section 6.1): query head h reads key/value head h // G,
+# query i sees keys i - left .. i + right (and j <= i when causal).
+
+
+def _band(S, causal, window):
+    wl, wr = window
+    i = np.arange(S)[:, None]
+    j = np.arange(S)[None, :]
+    m = np.ones((S, S), dtype=bool)
+    if causal:
+        m &= j <= i
+    if wl >= 0:
+        m &= j >= i - wl
+    if wr >= 0:
+        m &= j <= i + wr
+    return m
+
+
+def pin_gqa_equals_replication(orc):
+    """Grouped heads give exactly what K/V replicated to every query head give;
+    dK, dV of a shared head are the sums over its query heads."""
+    for causal in (False, True):
+        B, H, Hkv, S, D = 2, 6, 2, 11, 4
+        q, dout = _rand((B, H, S, D), 300), _rand((B, H, S, D), 301)
+        k, v = _rand((B, Hkv, S, D), 302), _rand((B, Hkv, S, D), 303)
+        kr, vr = np.repeat(k, H // Hkv, axis=1), np.repeat(v, H // Hkv, axis=1)
+        o1, l1 = orc.attention(q, k, v, causal, 0.6)
+        o2, l2 = orc.attention(q, kr, vr, causal, 0.6)
+        _close(o1, o2, 1e-14, "GQA O vs replicated K/V")
+        _close(l1, l2, 1e-14, "GQA lse vs replicated K/V")
+        g1 = orc.attention_bwd(q, k, v, dout, causal, 0.6)
+        g2 = orc.attention_bwd(q, kr, vr, dout, causal, 0.6)
+        _close(g1[0], g2[0], 1e-13, "GQA dQ")
+        for a, b, nm in ((g1[1], g2[1], "dK"), (g1[2], g2[2], "dV")):
+            _close(a, b.reshape(B, Hkv, H // Hkv, S, D).sum(axis=2), 1e-13, f"GQA {nm} = group sum")
+
+
+def pin_window_torch_reference(orc):
+    """Windowed (and grouped) attention against torch float64 softmax of a band-masked
+    score matrix, and its gradients against torch autograd."""
+    seed = 310
+    for causal, window in [(True, (3, -1)), (False, (2, 4)), (False, (0, 0)), (True, (0, 0)), (False, (-1, 1))]:
+        B, H, Hkv, S, D = 1, 4, 2, 12, 3
+        q, dout = _rand((B, H, S, D), seed), _rand((B, H, S, D), seed + 1)
+        k, v = _rand((B, Hkv, S, D), seed + 2), _rand((B, Hkv, S, D), seed + 3)
+        seed += 4
+        o, lse = orc.attention(q, k, v, causal, 0.7, window)
+        tq = torch.from_numpy(q.copy()).requires_grad_(True)
+        tk = torch.from_numpy(k.copy()).requires_grad_(True)
+        tv = torch.from_numpy(v.copy()).requires_grad_(True)
+        ke = tk.repeat_interleave(H // Hkv, dim=1)
+        ve = tv.repeat_interleave(H // Hkv, dim=1)
+        sc = torch.matmul(tq, ke.transpose(-1, -2)) * 0.7
+        sc = sc.masked_fill(~torch.from_numpy(_band(S, causal, window)), float("-inf"))
+        ref_o = torch.matmul(torch.softmax(sc, dim=-1), ve)
+        _close(o, ref_o.detach().numpy(), 1e-12, f"windowed O causal={causal} window={window}")
+        _close(lse, torch.logsumexp(sc, dim=-1).detach().numpy(), 1e-12, f"windowed lse {window}")
+        ref_o.backward(torch.from_numpy(dout))
+        dq, dk, dv = orc.attention_bwd(q, k, v, dout, causal, 0.7, window)
+        for nm, got, ref in (("dQ", dq, tq.grad), ("dK", dk, tk.grad), ("dV", dv, tv.grad)):
+            _close(got, ref.numpy(), 1e-12, f"windowed {nm} causal={causal} window={window}")
+
+
+def pin_window_limits(orc):
+    """A window wider than the sequence changes nothing; window (0, 0) leaves each
+    query its own key: O = V, lse = scale <q, k>, dV = dO, dQ = dK = 0."""
+    B, H, S, D = 2, 2, 9, 4
+    q, k, v, dout = (_rand((B, H, S, D), 330 + t) for t in range(4))
+    for causal in (False, True):
+        o1, l1 = orc.attention(q, k, v, causal, 0.5)
+        o2, l2 = orc.attention(q, k, v, causal, 0.5, (S, S))
+        _close(o2, o1, 0.0, "window wider than S, O")
+        _close(l2, l1, 0.0, "window wider than S, lse")
+        o, lse = orc.attention(q, k, v, causal, 0.5, (0, 0))
+        _close(o, v, 1e-15, "window (0,0) O = V")
+        _close(lse, 0.5 * np.sum(q * k, axis=-1), 1e-14, "window (0,0) lse")
+        dq, dk, dv = orc.attention_bwd(q, k, v, dout, causal, 0.5, (0, 0))
+        _close(dv, dout, 1e-15, "window (0,0) dV = dO")
+        _close(dq, np.zeros_like(dq), 1e-15, "window (0,0) dQ")
+        _close(dk, np.zeros_like(dk), 1e-15, "window (0,0) dK")
+
+
+def pin_window_reversal(orc):
+    """Reversing the sequence turns a (left, right) window into (right, left)."""
+    B, H, S, D = 1, 2, 14, 3
+    q, k, v = (_rand((B, H, S, D), 340 + t) for t in range(3))
+    o1, l1 = orc.attention(q, k, v, False, 0.8, (2, 5))
+    rev = (slice(None), slice(None), slice(None, None, -1))
+    o2, l2 = orc.attention(q[rev], k[rev], v[rev], False, 0.8, (5, 2))
+    _close(o2[rev], o1, 1e-13, "reversed window O")
+    _close(l2[rev], l1, 1e-13, "reversed window lse")
+
+
+def pin_window_finite_differences(orc):
+    """Windowed, grouped gradients against central differences of sum(dO * O)."""
+    B, H, Hkv, S, D = 1, 2, 1, 7, 2
+    q, dout = _rand((B, H, S, D), 350), _rand((B, H, S, D), 351)
+    k, v = _rand((B, Hkv, S, D), 352), _rand((B, Hkv, S, D), 353)
+    window, h = (2, 1), 1e-5
+    dq, dk, dv = orc.attention_bwd(q, k, v, dout, False, 0.9, window)
+    for name, x, got in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            vals = []
+            for step in (h, -h):
+                xs = x.copy()
+                xs[idx] += step
+                args = {"q": q, "k": k, "v": v}
+                args[name] = xs
+                o, _ = orc.attention(args["q"], args["k"], args["v"], False, 0.9, window)
+                vals.append(float(np.sum(o * dout)))
+            fd[idx] = (vals[0] - vals[1]) / (2 * h)
+        _close(got, fd, 1e-7, f"windowed grouped d{name} vs finite differences")
+
+
+def pin_ex_rows_entries(orc):
+    """With grouped heads and a window, the row entries equal the full entries
+    (dK, dV addressed by key/value rows)."""
+    B, H, Hkv, S, D = 2, 4, 2, 13, 3
+    q, dout = _rand((B, H, S, D), 360), _rand((B, H, S, D), 361)
+    k, v = _rand((B, Hkv, S, D), 362), _rand((B, Hkv, S, D), 363)
+    for causal, window in ((True, (4, -1)), (False, (3, 2))):
+        o, lse = orc.attention(q, k, v, causal, 0.4, window)
+        rows = np.array([0, 5, 12, 13, 30, B * H * S - 1], dtype=np.int64)
+        orow, lrow = orc.attention_rows(q, k, v, causal, 0.4, rows, window)
+        _close(orow, o.reshape(-1, D)[rows], 0.0, "ex rows O")
+        _close(lrow, lse.reshape(-1)[rows], 0.0, "ex rows lse")
+        dq, dk, dv = orc.attention_bwd(q, k, v, dout, causal, 0.4, window)
+        krows = np.array([0, 3, 12, 20, B * Hkv * S - 1], dtype=np.int64)
+        rq, rk, rv = orc.attention_bwd_rows(q, k, v, dout, causal, 0.4, rows, krows, window)
+        _close(rq, dq.reshape(-1, D)[rows], 1e-13, "ex rows dQ")
+        _close(rk, dk.reshape(-1, D)[krows], 1e-13, "ex rows dK")
+        _close(rv, dv.reshape(-1, D)[krows], 1e-13, "ex rows dV")
+
 ALL_PINS = [
     pin_worked_example,
     pin_normalisation,
@@ -420,4 +557,10 @@ ALL_PINS = [
     pin_bwd_single_key,
     pin_bwd_torch_autograd,
     pin_bwd_rows_entry,
+    pin_gqa_equals_replication,
+    pin_window_torch_reference,
+    pin_window_limits,
+    pin_window_reversal,
+    pin_window_finite_differences,
+    pin_ex_rows_entries,
 ]

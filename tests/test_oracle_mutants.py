@@ -22,12 +22,13 @@ MUTANTS = {
     "no_normalisation": ("o_i[d] = acc[d] / l;", "o_i[d] = acc[d];"),
     "lse_base2": ("*lse_i = m + log(l);", "*lse_i = m + log2(l);"),
     "lse_drops_max": ("*lse_i = m + log(l);", "*lse_i = log(l);"),
-    "causal_off_by_one": ("causal ? i + 1 : S", "causal ? (i > 0 ? i : 1) : S"),
-    "causal_wrong_triangle": ("causal ? i + 1 : S", "causal ? S - i : S"),
+    "causal_off_by_one": ("int64_t a = 0, b = causal ? i : S - 1;",
+                          "int64_t a = 0, b = causal ? (i > 0 ? i - 1 : 0) : S - 1;"),
+    "causal_wrong_triangle": ("int64_t a = 0, b = causal ? i : S - 1;", "int64_t a = causal ? i : 0, b = S - 1;"),
     "k_transposed": ("const double *k_j = k_bh + j * D;", "const double *k_j = k_bh + j;"),
     "v_transposed": ("const double *v_j = v_bh + j * D;", "const double *v_j = v_bh + j;"),
-    "k_head_offset_dropped": ("k + bh * S * D", "k"),
-    "v_head_offset_dropped": ("v + bh * S * D", "v"),
+    "k_head_offset_dropped": ("k + (kvh * S + lo) * D", "k + lo * D"),
+    "v_head_offset_dropped": ("v + (kvh * S + lo) * D", "v + lo * D"),
     "acc_init_one": ("acc[d] = 0.0;", "acc[d] = 1.0;"),
     "l_init_one": ("double l = 0.0;", "double l = 1.0;"),
     "q_row_offset": ("q + flat * D", "q + bh * S * D"),
@@ -36,17 +37,26 @@ MUTANTS = {
     "bwd_ds_without_p": ("const double ds = w[j] * (g[j] - row);", "const double ds = g[j] - row;"),
     "bwd_row_term_sign": ("const double ds = w[j] * (g[j] - row);", "const double ds = w[j] * (g[j] + row);"),
     "bwd_dq_no_scale": ("dq_i[d] += scale * ds * kr[d];", "dq_i[d] += ds * kr[d];"),
-    "bwd_dq_uses_v": ("dq_i[d] += scale * ds * kr[d];", "dq_i[d] += scale * ds * v_bh[j * D + d];"),
+    "bwd_dq_uses_v": ("dq_i[d] += scale * ds * kr[d];", "dq_i[d] += scale * ds * v_h[(lo + j) * D + d];"),
     "bwd_dk_uses_k": ("dk_j[d] += scale * ds * q_i[d];", "dk_j[d] += scale * ds * kr[d];"),
     "bwd_dv_uses_ds": ("dv_j[d] += w[j] * do_i[d];", "dv_j[d] += ds * do_i[d];"),
     "bwd_dv_wrong_index": ("dv_j[d] += w[j] * do_i[d];", "dv_j[d] += w[j] * do_i[0];"),
     "bwd_dp_wrong_row": ("const double *vr = v_bh + j * D;", "const double *vr = v_bh;"),
     "bwd_unnormalised_p": ("w[j] /= total;", "w[j] /= 1.0;"),
-    "bwd_causal_sees_all": ("const int64_t n_keys = causal ? i + 1 : S;\n        const double *q_i = q_bh + i * D;",
-                            "const int64_t n_keys = S;\n        const double *q_i = q_bh + i * D;"),
+    "bwd_causal_sees_all": ("key_range(i, S, causal, wl, wr, &lo, &hi);\n            const int64_t n_keys = hi - lo + 1;\n            const double *q_i = q_g",
+                            "key_range(i, S, 0, wl, wr, &lo, &hi);\n            const int64_t n_keys = hi - lo + 1;\n            const double *q_i = q_g"),
     "bwd_rows_p_not_normalised": ("const double p = exp(scale * acc - top[x]) / sum[x];",
                                   "const double p = exp(scale * acc - top[x]);"),
-    "bwd_rows_key_range": ("for (int64_t i = causal ? t : 0; i < S; ++i) {", "for (int64_t i = 0; i < S; ++i) {"),
+    "bwd_rows_key_range": ("if (t < lo || t > hi)", "if (t < lo)"),
+    "bwd_rows_ignores_left_window": ("if (t < lo || t > hi)", "if (t > hi)"),
+    # grouped heads and windows
+    "kv_head_interleaved": ("return bh / (H / Hkv);", "return bh % Hkv;"),
+    "window_left_off_by_one": ("if (wl >= 0 && i - wl > a)\n        a = i - wl;",
+                               "if (wl >= 0 && i - wl + 1 > a)\n        a = i - wl + 1;"),
+    "window_right_ignored": ("if (wr >= 0 && i + wr < b)\n        b = i + wr;", ""),
+    "window_sides_swapped": ("if (wl >= 0 && i - wl > a)", "if (wr >= 0 && i - wr > a)"),
+    "bwd_group_not_summed": ("for (int64_t hq = 0; hq < G; ++hq) {\n        for (int64_t i = 0; i < S; ++i) {",
+                             "for (int64_t hq = G - 1; hq < G; ++hq) {\n        for (int64_t i = 0; i < S; ++i) {"),
 }
 
 
