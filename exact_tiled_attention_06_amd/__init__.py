@@ -13,11 +13,13 @@ import this package before the library exists.
         the C backward entry point;
     fa_status_string(status)
         the C status description;
-    forward(q, k, v, causal=False, scale=None) -> (o, lse)
+    forward(q, k, v, causal=False, scale=None, window=None) -> (o, lse)
         convenience on torch tensors [B,H,S,D]: allocates o (input dtype) and
         lse (float32 [B,H,S]) and calls fa_fwd on the current stream.  The
         default scale is 1/sqrt(D) ("T5 讲解：FlashAttention forward", section ⑥).
-    backward(q, k, v, o, lse, dout, causal=False, scale=None) -> (dq, dk, dv)
+    fa_fwd_ex / fa_bwd_ex(...)
+        the C entry points with grouped K/V heads (H_kv) and a sliding window;
+    backward(q, k, v, o, lse, dout, causal=False, scale=None, window=None) -> (dq, dk, dv)
         gradients for the upstream gradient dout, from the forward's o and lse;
         allocates the outputs and the D workspace and calls fa_bwd.
 """
@@ -43,6 +45,7 @@ FA_ERR_ALIAS = 7
 FA_ERR_TOO_LARGE = 8
 FA_ERR_LAUNCH = 9
 FA_ERR_ALIGNMENT = 10
+FA_ERR_WINDOW = 11
 
 FA_DTYPE_F32 = 0
 FA_DTYPE_F16 = 1
@@ -52,7 +55,7 @@ DTYPE_CODES = {torch.float32: FA_DTYPE_F32, torch.float16: FA_DTYPE_F16, torch.b
 
 # argument problems map to ValueError, runtime problems to RuntimeError
 _VALUE_ERRORS = {FA_ERR_NULL_POINTER, FA_ERR_SHAPE, FA_ERR_HEAD_DIM, FA_ERR_DTYPE, FA_ERR_CAUSAL,
-                 FA_ERR_SCALE, FA_ERR_ALIAS, FA_ERR_TOO_LARGE, FA_ERR_ALIGNMENT}
+                 FA_ERR_SCALE, FA_ERR_ALIAS, FA_ERR_TOO_LARGE, FA_ERR_ALIGNMENT, FA_ERR_WINDOW}
 
 
 def _load() -> ctypes.CDLL:
@@ -67,6 +70,11 @@ def _load() -> ctypes.CDLL:
     lib.fa_bwd.restype = ctypes.c_int
     lib.fa_bwd.argtypes = [ctypes.c_void_p] * 10 + [ctypes.c_int64] * 4 + [
         ctypes.c_int, ctypes.c_float, ctypes.c_int, ctypes.c_void_p]
+    I64, I, F, P = ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_void_p
+    lib.fa_fwd_ex.restype = I
+    lib.fa_fwd_ex.argtypes = [P] * 5 + [I64] * 5 + [I, I64, I64, F, I, P]
+    lib.fa_bwd_ex.restype = I
+    lib.fa_bwd_ex.argtypes = [P] * 10 + [I64] * 5 + [I, I64, I64, F, I, P]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_status_string.argtypes = [ctypes.c_int]
     return lib
@@ -113,6 +121,35 @@ def fa_bwd(q: int, k: int, v: int, o: int, dout: int, lse: int, dq: int, dk: int
                                 float(scale), int(dtype), stream))
 
 
+def fa_fwd_ex(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, H_kv: int, S: int, D: int,
+              causal: int, window_left: int, window_right: int, scale: float, dtype: int, stream: int) -> int:
+    """The C forward with grouped K/V heads and a sliding window; returns the status code."""
+    return int(library().fa_fwd_ex(q, k, v, o, lse, B, H, H_kv, S, D, int(causal), int(window_left),
+                                   int(window_right), float(scale), int(dtype), stream))
+
+
+def fa_bwd_ex(q: int, k: int, v: int, o: int, dout: int, lse: int, dq: int, dk: int, dv: int, delta: int,
+              B: int, H: int, H_kv: int, S: int, D: int, causal: int, window_left: int, window_right: int,
+              scale: float, dtype: int, stream: int) -> int:
+    """The C backward with grouped K/V heads and a sliding window; returns the status code."""
+    return int(library().fa_bwd_ex(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, H_kv, S, D, int(causal),
+                                   int(window_left), int(window_right), float(scale), int(dtype), stream))
+
+
+def _window(window):
+    if window is None:
+        return -1, -1
+    wl, wr = int(window[0]), int(window[1])
+    return wl, wr
+
+
+def _kv_shape_ok(q: torch.Tensor, k: torch.Tensor) -> bool:
+    if k.dim() != 4 or k.shape[0] != q.shape[0] or k.shape[2:] != q.shape[2:]:
+        return False
+    hq, hk = q.shape[1], k.shape[1]
+    return (hq == 0 and hk == 0) or (hk >= 1 and hq % hk == 0)
+
+
 def check(status: int) -> None:
     if status == FA_OK:
         return
@@ -123,12 +160,15 @@ def check(status: int) -> None:
 
 def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
             scale: float | None = None, out: torch.Tensor | None = None,
-            lse: torch.Tensor | None = None):
-    """Attention forward on [B,H,S,D] device tensors; returns (o, lse)."""
+            lse: torch.Tensor | None = None, window=None):
+    """Attention forward on device tensors q [B,H,S,D], k and v [B,H_kv,S,D]
+    (H a multiple of H_kv); returns (o, lse).  ``window = (left, right)`` limits
+    query i to keys i - left .. i + right (-1: unlimited side)."""
     if q.dim() != 4:
         raise ValueError(f"q must be [B,H,S,D], got shape {tuple(q.shape)}")
-    if k.shape != q.shape or v.shape != q.shape:
-        raise ValueError(f"q, k, v shapes differ: {tuple(q.shape)}, {tuple(k.shape)}, {tuple(v.shape)}")
+    if not _kv_shape_ok(q, k) or v.shape != k.shape:
+        raise ValueError(f"k, v must share a [B,H_kv,S,D] shape with H a multiple of H_kv: "
+                         f"{tuple(q.shape)}, {tuple(k.shape)}, {tuple(v.shape)}")
     if not (q.dtype == k.dtype == v.dtype) or q.dtype not in DTYPE_CODES:
         raise ValueError(f"q, k, v must share one of {list(DTYPE_CODES)}; got {q.dtype}, {k.dtype}, {v.dtype}")
     if not (q.is_cuda and k.is_cuda and v.is_cuda):
@@ -148,21 +188,23 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = Fa
     if lse.shape != (B, H, S) or lse.dtype != torch.float32 or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 tensor of shape [B,H,S]")
     stream = torch.cuda.current_stream(q.device).cuda_stream
-    status = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                    B, H, S, D, int(bool(causal)), scale, DTYPE_CODES[q.dtype], stream)
+    wl, wr = _window(window)
+    status = fa_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                       B, H, k.shape[1], S, D, int(bool(causal)), wl, wr, scale, DTYPE_CODES[q.dtype], stream)
     check(status)
     return out, lse
 
 
 def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
-             dout: torch.Tensor, causal: bool = False, scale: float | None = None):
-    """Attention backward on [B,H,S,D] device tensors (fp16 / bf16): returns (dq, dk, dv).
+             dout: torch.Tensor, causal: bool = False, scale: float | None = None, window=None):
+    """Attention backward (fp16 / bf16): returns (dq, dk, dv), dk and dv shaped like k.
 
-    o and lse are the forward's outputs for the same q, k, v, causal and scale;
-    the D = rowsum(dout * o) workspace is allocated here."""
+    q, o, dout are [B,H,S,D], k and v [B,H_kv,S,D]; o and lse are the forward's
+    outputs for the same q, k, v, causal, scale and window; the
+    D = rowsum(dout * o) workspace is allocated here."""
     ts = (q, k, v, o, dout)
-    if q.dim() != 4 or any(t.shape != q.shape for t in ts):
-        raise ValueError(f"q, k, v, o, dout must share one [B,H,S,D] shape")
+    if q.dim() != 4 or o.shape != q.shape or dout.shape != q.shape or not _kv_shape_ok(q, k) or v.shape != k.shape:
+        raise ValueError("q, o, dout must share one [B,H,S,D] shape and k, v one [B,H_kv,S,D] shape")
     if any(t.dtype != q.dtype for t in ts) or q.dtype not in (torch.float16, torch.bfloat16):
         raise ValueError("q, k, v, o, dout must share dtype float16 or bfloat16")
     if not all(t.is_cuda for t in ts + (lse,)):
@@ -175,11 +217,12 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     scale = float(torch.tensor(scale, dtype=torch.float32))
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(k)
     delta = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
     stream = torch.cuda.current_stream(q.device).cuda_stream
-    status = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
-                    dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), B, H, S, D,
-                    int(bool(causal)), scale, DTYPE_CODES[q.dtype], stream)
+    wl, wr = _window(window)
+    status = fa_bwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+                       dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), B, H, k.shape[1], S, D,
+                       int(bool(causal)), wl, wr, scale, DTYPE_CODES[q.dtype], stream)
     check(status)
     return dq, dk, dv

@@ -125,8 +125,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(Cfg::NT, Cfg::NT), amdgpu_
 void fa_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                       const uint16_t* __restrict__ V, const uint16_t* __restrict__ O,
                       const uint16_t* __restrict__ dO, const float* __restrict__ LSE,
-                      uint16_t* __restrict__ dQ, float* __restrict__ DELTA, int S, int BH, int n_blk, float c,
-                      float scale) {
+                      uint16_t* __restrict__ dQ, float* __restrict__ DELTA, int S, int BH, int n_blk, int G,
+                      int wl, int wr, float c, float scale) {
     using L = typename Cfg::L;
     using W = WaveTile<T, L>;
     constexpr int D = Cfg::D, KS = Cfg::KS, DB = Cfg::DB, RB = Cfg::RB, BM = Cfg::BM;
@@ -159,16 +159,26 @@ void fa_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict
     const int qw = q0 + 32 * wave;
 
     const int64_t head = (int64_t)bh * S * D;
-    const __amdgpu_buffer_rsrc_t krs = head_rsrc<T>(K + head, S * RB);
-    const __amdgpu_buffer_rsrc_t vrs = head_rsrc<T>(V + head, S * RB);
+    const int64_t kvhead = (int64_t)(bh / G) * S * D;  // grouped heads: G query heads per K/V head
+    const __amdgpu_buffer_rsrc_t krs = head_rsrc<T>(K + kvhead, S * RB);
+    const __amdgpu_buffer_rsrc_t vrs = head_rsrc<T>(V + kvhead, S * RB);
     const uint32_t roff = tile_lane_offset<L, false>(wave, lane);
     const uint32_t toff = tile_lane_offset<L, true>(wave, lane);
 
-    const int ntiles = ((CAUSAL ? min(q0 + BM, S) : S) + 31) / 32;
-    const int wt = qw < S ? min(ntiles, ((CAUSAL ? min(qw + 32, S) : S) + 31) / 32) : 0;
-    const int um = min(CAUSAL ? (qw + 1) / 32 : ntiles, S / 32);
+    // keys of query i: lo(i) .. hi(i) (causal: up to i; window: i - wl .. i + wr)
+    auto lo_of = [&](int i) { return wl >= 0 ? max(0, i - wl) : 0; };
+    auto hi_of = [&](int i) { return min(CAUSAL ? i : S - 1, wr >= 0 ? i + wr : S - 1); };
+    const int qlast = min(q0 + BM, S) - 1;
+    const int tb = lo_of(q0) / 32;                 // the workgroup's key tiles [tb, te)
+    const int te = hi_of(qlast) / 32 + 1;
+    const bool live = qw < S;
+    const int wlast = min(qw + 31, S - 1);
+    const int wb = live ? lo_of(qw) / 32 : te;      // this wave's tiles [wb, we)
+    const int we = live ? hi_of(wlast) / 32 + 1 : te;
+    const int ml = (lo_of(wlast) + 31) / 32;        // tiles in [ml, mu) need no mask
+    const int mu = (hi_of(qw) + 1) / 32;
     const int qrow = min(qw + n, S - 1);
-    const int last = CAUSAL ? qrow : S - 1;
+    const int first = lo_of(qrow), last = hi_of(qrow);
 
     auto stage = [&](auto par, int t) __attribute__((always_inline)) {
         constexpr int P = decltype(par)::value;
@@ -178,7 +188,7 @@ void fa_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict
     };
     using P0 = std::integral_constant<int, 0>;
     using P1 = std::integral_constant<int, 1>;
-    if (ntiles > 0) stage(P0{}, 0);
+    stage(P0{}, tb);
 
     // resident: Q and dO fragments of the wave's 32 queries; D = rowsum(dO o O)
     u32x4 qf[KS], df[KS];
@@ -209,8 +219,8 @@ void fa_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict
         constexpr int P = decltype(par)::value;
         wait_vmcnt0();
         __syncthreads();
-        if (t + 1 < ntiles) stage(std::integral_constant<int, 1 - P>{}, t + 1);
-        if (t >= wt) return;
+        if (t + 1 < te) stage(std::integral_constant<int, 1 - P>{}, t + 1);
+        if (t < wb || t >= we) return;
         const f32x16 zero = {};
         f32x16 st = zero, dpt = zero;
 #pragma unroll
@@ -218,12 +228,14 @@ void fa_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict
             st = mfma32x32x16<T>(W::k_frag(krb[P], offk, 0, ks), qf[ks], ks == 0 ? zero : st);
             dpt = mfma32x32x16<T>(W::k_frag(vrb[P], offk, 0, ks), df[ks], ks == 0 ? zero : dpt);
         }
-        if (t >= um) {
-            // key of register r: 32t + 8(r/4) + 4h + r%4, visible iff <= last
-            const int lim = last - (t * 32 + 4 * h);
+        if (t < ml || t >= mu) {
+            // key of register r: 32t + 8(r/4) + 4h + r%4, visible iff first <= key <= last
+            const int k0 = t * 32 + 4 * h;
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-                if (8 * (r >> 2) + (r & 3) > lim) st[r] = kNegInf;
+            for (int r = 0; r < 16; ++r) {
+                const int key = k0 + 8 * (r >> 2) + (r & 3);
+                if (key < first || key > last) st[r] = kNegInf;
+            }
         }
         u32x4 dsp[2];
 #pragma unroll
@@ -238,12 +250,12 @@ void fa_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict
             for (int db = 0; db < DB; ++db)
                 dqacc[db] = mfma32x32x16<T>(W::v_frag(ktb[P], offv, 0, j, db), dsp[j], dqacc[db]);
     };
-    int t = 0;
-    for (; t + 1 < ntiles; t += 2) {
+    int t = tb;
+    for (; t + 1 < te; t += 2) {
         step(P0{}, t);
         step(P1{}, t + 1);
     }
-    if (t < ntiles) step(P0{}, t);
+    if (t < te) step(P0{}, t);
 
     if (qw + n < S) store_t<T, D, DB>(dQ + head, qw + n, h, dqacc, scale);
 }
@@ -255,7 +267,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(Cfg::NT, Cfg::NT), amdgpu_
 void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                         const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
                         const float* __restrict__ LSE, const float* __restrict__ DELTA,
-                        uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int S, int BH, int n_blk, float scale) {
+                        uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int S, int BHkv, int n_blk, int G,
+                        int wl, int wr, float scale) {
     using L = typename Cfg::L;
     using W = WaveTile<T, L>;
     constexpr int D = Cfg::D, KS = Cfg::KS, DB = Cfg::DB, RB = Cfg::RB, BM = Cfg::BM;
@@ -289,28 +302,44 @@ void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
     const int n = lane & 31;
     const int h = lane >> 5;
 
-    // heads vary fastest; causal key blocks with the most queries (lowest
-    // keys) first
+    // K/V heads vary fastest; causal key blocks with the most queries (lowest
+    // keys) first.  The workgroup owns keys k0 .. k0+BM-1 of K/V head kvbh and
+    // walks, for each of the G query heads that read it, the query tiles that
+    // can see any of its keys.
     const int wg = blockIdx.x;
-    const int bh = wg % BH;
-    const int kblk = wg / BH;
+    const int kvbh = wg % BHkv;
+    const int kblk = wg / BHkv;
     const int k0 = kblk * BM;
     const int kw = k0 + 32 * wave;
 
-    const int64_t head = (int64_t)bh * S * D;
-    const __amdgpu_buffer_rsrc_t qrs = head_rsrc<T>(Q + head, S * RB);
-    const __amdgpu_buffer_rsrc_t ors = head_rsrc<T>(dO + head, S * RB);
+    const int64_t kvhead = (int64_t)kvbh * S * D;
     const uint32_t roff = tile_lane_offset<L, false>(wave, lane);
     const uint32_t toff = tile_lane_offset<L, true>(wave, lane);
 
-    const int nq = (S + 31) / 32;                    // query tiles of the head
-    const int t0 = CAUSAL ? k0 / 32 : 0;             // first query tile any key here sees
-    const int tw = CAUSAL ? kw / 32 : 0;             // this wave's first query tile
+    // queries that see key j: ilo(j) .. ihi(j) (causal: from j; window: j - wr .. j + wl)
+    auto ilo_of = [&](int j) { return max(CAUSAL ? j : 0, wr >= 0 ? j - wr : 0); };
+    auto ihi_of = [&](int j) { return min(S - 1, wl >= 0 ? j + wl : S - 1); };
+    const int klast = min(k0 + BM, S) - 1;
+    const int t0 = ilo_of(k0) / 32;                  // query tiles [t0, t1) of each head
+    const int t1 = ihi_of(klast) / 32 + 1;
+    const int nt = t1 - t0;
+    const int nsteps = G * nt;
     const bool live = kw < S;                        // the wave has keys
-    const bool ragged = (S % 32) != 0;               // last query tile has rows past S
+    const int kwlast = min(kw + 31, S - 1);
+    const int tw0 = live ? ilo_of(kw) / 32 : t1;     // this wave's query tiles [tw0, tw1)
+    const int tw1 = live ? ihi_of(kwlast) / 32 + 1 : t1;
+    const int ml = (ilo_of(kwlast) + 31) / 32;       // query tiles in [ml, mu) need no mask
+    const int mu = (ihi_of(kw) + 1) / 32;
+    const int krow = min(kw + n, S - 1);
+    const int qlo = ilo_of(krow), qhi = ihi_of(krow);  // this lane's key is seen by qlo .. qhi
 
-    auto stage = [&](auto par, int t) __attribute__((always_inline)) {
+    // step u: query head kvbh*G + u / nt, query tile t0 + u % nt
+    auto stage = [&](auto par, int u) __attribute__((always_inline)) {
         constexpr int P = decltype(par)::value;
+        const int64_t qhead = (int64_t)(kvbh * G + u / nt) * S * D;
+        const int t = t0 + u % nt;
+        const __amdgpu_buffer_rsrc_t qrs = head_rsrc<T>(Q + qhead, S * RB);
+        const __amdgpu_buffer_rsrc_t ors = head_rsrc<T>(dO + qhead, S * RB);
         load_tile<T, L, false>(qrb[P], qrs, roff, t * 32, wave, lane);
         load_tile<T, L, true>(qtb[P], qrs, toff, t * 32, wave, lane);
         load_tile<T, L, false>(orb[P], ors, roff, t * 32, wave, lane);
@@ -322,11 +351,12 @@ void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
     // 0 and are masked.
     float lreg = 0.f, dreg = 0.f;
     const bool ld_lane = wave == 0 && lane < 32;
-    auto fetch_ld = [&](int t) __attribute__((always_inline)) {
-        const int row = t * 32 + lane;
+    auto fetch_ld = [&](int u) __attribute__((always_inline)) {
+        const int64_t qrow0 = (int64_t)(kvbh * G + u / nt) * S;
+        const int row = (t0 + u % nt) * 32 + lane;
         if (ld_lane && row < S) {
-            lreg = LSE[(int64_t)bh * S + row];
-            dreg = DELTA[(int64_t)bh * S + row];
+            lreg = LSE[qrow0 + row];
+            dreg = DELTA[qrow0 + row];
         } else {
             lreg = 0.f;
             dreg = 0.f;
@@ -334,16 +364,13 @@ void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
     };
     using P0 = std::integral_constant<int, 0>;
     using P1 = std::integral_constant<int, 1>;
-    if (t0 < nq) {
-        stage(P0{}, t0);
-        fetch_ld(t0);
-    }
+    stage(P0{}, 0);
+    fetch_ld(0);
 
     // resident: K and V fragments of the wave's 32 keys
-    const int krow = min(kw + n, S - 1);
     u32x4 kf[KS], vf[KS];
-    row_frags<KS>(K + head, krow, D, h, kf);
-    row_frags<KS>(V + head, krow, D, h, vf);
+    row_frags<KS>(K + kvhead, krow, D, h, kf);
+    row_frags<KS>(V + kvhead, krow, D, h, vf);
 
     int offk[KS], offv[DB];
     frag_offsets<L>(lane, offk, offv);
@@ -357,8 +384,8 @@ void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
             dvacc[db][r] = 0.f;
         }
 
-    // query tile t, buffers of parity (t - t0) % 2
-    auto step = [&](auto par, int t) __attribute__((always_inline)) {
+    // step u, buffers of parity u % 2
+    auto step = [&](auto par, int u) __attribute__((always_inline)) {
         constexpr int P = decltype(par)::value;
         wait_vmcnt0();
         if (ld_lane) {
@@ -366,11 +393,12 @@ void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
             dlb[P][lane] = dreg;
         }
         __syncthreads();
-        if (t + 1 < nq) {
-            stage(std::integral_constant<int, 1 - P>{}, t + 1);
-            fetch_ld(t + 1);
+        if (u + 1 < nsteps) {
+            stage(std::integral_constant<int, 1 - P>{}, u + 1);
+            fetch_ld(u + 1);
         }
-        if (!live || t < tw) return;
+        const int t = t0 + u % nt;
+        if (t < tw0 || t >= tw1) return;  // wave-uniform
         const f32x16 zero = {};
         f32x16 s = zero, dp = zero;
 #pragma unroll
@@ -393,10 +421,9 @@ void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
                 dd[4 * g + e] = b[e];
             }
         }
-        // visible iff query >= key (causal, only the diagonal tile t == tw
-        // has both) and query < S (only the last tile when S % 32 != 0)
-        const bool diag = CAUSAL && t == tw;
-        const bool tail = ragged && t == nq - 1;
+        // queries outside qlo .. qhi (which ends before S) do not see this
+        // lane's key: only tiles outside [ml, mu) have any
+        const bool edge = t < ml || t >= mu;
         u32x4 pp[2], dsp[2];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -404,8 +431,8 @@ void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
                 const int r = 2 * i + e;
-                const int rr = 8 * (r >> 2) + 4 * h + (r & 3);
-                const bool hide = (diag & (rr < n)) | (tail & (t * 32 + rr >= S));
+                const int q = t * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                const bool hide = edge & ((q < qlo) | (q > qhi));
                 const float p = hide ? 0.f : exp2_fast(kLog2e * __builtin_fmaf(s[r], scale, -lse[r]));
                 pv[e] = p;
                 dv[e] = p * (dp[r] - dd[r]);
@@ -421,16 +448,16 @@ void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
                 dkacc[db] = mfma32x32x16<T>(W::v_frag(qtb[P], offv, 0, j, db), dsp[j], dkacc[db]);
             }
     };
-    int t = t0;
-    for (; t + 1 < nq; t += 2) {
-        step(P0{}, t);
-        step(P1{}, t + 1);
+    int u = 0;
+    for (; u + 1 < nsteps; u += 2) {
+        step(P0{}, u);
+        step(P1{}, u + 1);
     }
-    if (t < nq) step(P0{}, t);
+    if (u < nsteps) step(P0{}, u);
 
     if (live && kw + n < S) {
-        store_t<T, D, DB>(dK + head, kw + n, h, dkacc, scale);
-        store_t<T, D, DB>(dV + head, kw + n, h, dvacc, 1.0f);
+        store_t<T, D, DB>(dK + kvhead, kw + n, h, dkacc, scale);
+        store_t<T, D, DB>(dV + kvhead, kw + n, h, dvacc, 1.0f);
     }
 }
 

@@ -14,7 +14,9 @@
 // the saved lse enables: "T5 讲解", section ⑥), and wave 0 writes O and lse.
 // Causal workgroups stop at their last row's diagonal and mask only the keys
 // that cross it ("Triton 实现", section "Causal Mask 的处理"; "T5 讲解",
-// section ⑤).
+// section ⑤); a sliding window (left, right) narrows every row's keys to
+// i - left .. i + right the same way, and grouped heads read K/V head bh / G
+// ("Inside FlashAttention", section 6.1).
 #pragma once
 
 #include "fa_common.hpp"
@@ -39,7 +41,7 @@ template <int D, bool CAUSAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(F32Cfg<D>::NT, F32Cfg<D>::NT)))
 void fa_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                        const float* __restrict__ V, float* __restrict__ O, float* __restrict__ LSE,
-                       int S, int BH, int n_qblk, float c) {
+                       int S, int BH, int n_qblk, int G, int wl, int wr, float c) {
     constexpr int NW = F32Cfg<D>::NW;
     constexpr int XW = D + 2;  // floats per lane in the merge: acc, m, l
     __shared__ float xch[(NW - 1) * XW * 64];
@@ -54,8 +56,9 @@ void fa_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
     const int q0 = qblk * F32_BM;
     const int qrow = q0 + lane;
     const int64_t head = (int64_t)bh * S * D;
-    const float* kh = K + head;
-    const float* vh = V + head;
+    const int64_t kvhead = (int64_t)(bh / G) * S * D;  // grouped heads: G query heads per K/V head
+    const float* kh = K + kvhead;
+    const float* vh = V + kvhead;
 
     float q[D], acc[D];
     const int qsrc = min(qrow, S - 1);
@@ -66,10 +69,17 @@ void fa_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
     }
     float m_run = kMInit, l_run = 0.f;
 
-    // this wave's slice [kb, ke) of the block's keys
-    const int kend = CAUSAL ? min(q0 + F32_BM, S) : S;
-    const int kb = wave * kend / NW;
-    const int ke = (wave + 1) * kend / NW;
+    // Keys of row i: lo(i) .. hi(i) -- at most i when causal, i - wl .. i + wr
+    // within a window (wl, wr = -1: no limit on that side).  The block's rows
+    // together see klo .. khi; this wave takes the slice [kb, ke) of it.
+    const int qlast = min(q0 + F32_BM, S) - 1;
+    const int klo = wl >= 0 ? max(0, q0 - wl) : 0;
+    const int khi = min(CAUSAL ? qlast : S - 1, wr >= 0 ? qlast + wr : S - 1);
+    const int nk = khi - klo + 1;
+    const int kb = klo + wave * nk / NW;
+    const int ke = klo + (wave + 1) * nk / NW;
+    const int lo = wl >= 0 ? max(0, qrow - wl) : 0;
+    const int hi = min(CAUSAL ? qrow : S - 1, wr >= 0 ? qrow + wr : S - 1);
     for (int key = kb; key < ke; ++key) {
         const float* kr = kh + (int64_t)key * D;
         float part[8];
@@ -78,7 +88,7 @@ void fa_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
 #pragma unroll
         for (int d = 0; d < D; ++d) part[d & 7] = __builtin_fmaf(q[d], kr[d], part[d & 7]);
         float sc = (((part[0] + part[1]) + (part[2] + part[3])) + ((part[4] + part[5]) + (part[6] + part[7]))) * c;
-        if (CAUSAL && key > qrow) sc = kNegInf;
+        if (key < lo || key > hi) sc = kNegInf;
         // move the reference only when a weight would exceed 2^kF32Margin
         if (__builtin_amdgcn_ballot_w64(sc > m_run + kF32Margin)) {
             const float m_new = fmaxf(m_run, sc);

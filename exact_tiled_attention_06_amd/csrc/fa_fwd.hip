@@ -17,6 +17,7 @@
 #include "fa_ksplit.hpp"
 #include "fa_split.hpp"
 #include "fa_bwd.hpp"
+#include "fa_window.hpp"
 
 #ifndef FA_SPLIT_TBN
 #define FA_SPLIT_TBN 128
@@ -59,119 +60,147 @@ bool overlaps(const void* a, int64_t na, const void* b, int64_t nb) {
     return a0 < b0 + (uintptr_t)nb && b0 < a0 + (uintptr_t)na;
 }
 
+// One forward call's device arguments and launch parameters.
+struct Fwd {
+    const void *q, *k, *v;
+    void* o;
+    float* lse;
+    int S, BH, G;  // G query heads per K/V head
+    int wl, wr;    // window (left, right); -1: no limit on that side
+    float c;       // scale * log2(e)
+    hipStream_t stream;
+};
+
 template <typename T, typename Cfg>
-int launch_cfg(const void* q, const void* k, const void* v, void* o, float* lse, int S, int BH, float c,
-               hipStream_t stream) {
-    const int n_qblk = (S + Cfg::BM - 1) / Cfg::BM;
-    const int64_t grid = (int64_t)n_qblk * BH;
+int launch_cfg(const Fwd& a) {
+    const int n_qblk = (a.S + Cfg::BM - 1) / Cfg::BM;
+    const int64_t grid = (int64_t)n_qblk * a.BH;
     if (grid > (int64_t)1 << 24) return FA_ERR_TOO_LARGE;
     (void)hipGetLastError();  // clear a stale error so the check below sees this launch only
     if constexpr (Cfg::QB == 2 && Cfg::KB == 1 && Cfg::PIPE)
-        hipLaunchKernelGGL((fa_fwd_split_kernel<T, Cfg>), dim3((unsigned)grid), dim3(Cfg::NT), 0, stream,
-                           (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse,
-                           S, BH, n_qblk, c);
+        hipLaunchKernelGGL((fa_fwd_split_kernel<T, Cfg>), dim3((unsigned)grid), dim3(Cfg::NT), 0, a.stream,
+                           (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o,
+                           a.lse, a.S, a.BH, n_qblk, a.G, a.c);
     else
-        hipLaunchKernelGGL((fa_fwd_mfma_kernel<T, Cfg>), dim3((unsigned)grid), dim3(Cfg::NT), 0, stream,
-                           (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse,
-                           S, BH, n_qblk, c);
+        hipLaunchKernelGGL((fa_fwd_mfma_kernel<T, Cfg>), dim3((unsigned)grid), dim3(Cfg::NT), 0, a.stream,
+                           (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o,
+                           a.lse, a.S, a.BH, n_qblk, a.G, a.c);
     return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
 // Thin grids: workgroups of NW waves that share BMW query rows and split the keys.
 template <typename T, typename Cfg>
-int launch_ksplit(const void* q, const void* k, const void* v, void* o, float* lse, int S, int BH, float c,
-                  hipStream_t stream) {
-    const int n_qblk = (S + Cfg::BMW - 1) / Cfg::BMW;
-    const int64_t grid = (int64_t)n_qblk * BH;
+int launch_ksplit(const Fwd& a) {
+    const int n_qblk = (a.S + Cfg::BMW - 1) / Cfg::BMW;
+    const int64_t grid = (int64_t)n_qblk * a.BH;
     if (grid > (int64_t)1 << 24) return FA_ERR_TOO_LARGE;
     (void)hipGetLastError();
-    hipLaunchKernelGGL((fa_fwd_ksplit_kernel<T, Cfg>), dim3((unsigned)grid), dim3(Cfg::NT), 0, stream,
-                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, S, BH, n_qblk,
-                       c);
+    hipLaunchKernelGGL((fa_fwd_ksplit_kernel<T, Cfg>), dim3((unsigned)grid), dim3(Cfg::NT), 0, a.stream,
+                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse,
+                       a.S, a.BH, n_qblk, a.G, a.c);
+    return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+// Sliding windows: 4 waves of 32 query rows, one 32-key tile per barrier.
+template <typename T, int D, bool CAUSAL>
+int launch_window(const Fwd& a) {
+    using Cfg = MfmaConfig<D, CAUSAL, 1, 4, 32, false, 2, 32>;
+    const int n_qblk = (a.S + Cfg::BM - 1) / Cfg::BM;
+    const int64_t grid = (int64_t)n_qblk * a.BH;
+    if (grid > (int64_t)1 << 24) return FA_ERR_TOO_LARGE;
+    (void)hipGetLastError();
+    hipLaunchKernelGGL((fa_fwd_window_kernel<T, Cfg>), dim3((unsigned)grid), dim3(Cfg::NT), 0, a.stream,
+                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse,
+                       a.S, a.BH, n_qblk, a.G, a.wl, a.wr, a.c);
     return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
 template <typename T, int D, bool CAUSAL>
-int launch_mfma(const void* q, const void* k, const void* v, void* o, float* lse, int S, int BH,
-                float c, hipStream_t stream) {
+int launch_mfma(const Fwd& a) {
+    if (a.wl >= 0 || a.wr >= 0) return launch_window<T, D, CAUSAL>(a);
     using TL = Tiles<D>;
     using Large = MfmaConfig<D, CAUSAL, TL::QB, TL::NW, TL::BN, TL::PIPE, 2, TL::TBN>;
     using Small = MfmaConfig<D, CAUSAL, TL::SMALL_QB, TL::SMALL_NW, TL::SMALL_BN, TL::SMALL_PIPE>;
-    const int64_t large_grid = (int64_t)((S + Large::BM - 1) / Large::BM) * BH;
-    if (large_grid >= kFullGrid) return launch_cfg<T, Large>(q, k, v, o, lse, S, BH, c, stream);
+    const int64_t large_grid = (int64_t)((a.S + Large::BM - 1) / Large::BM) * a.BH;
+    if (large_grid >= kFullGrid) return launch_cfg<T, Large>(a);
     if constexpr (D <= 64) {
         // 64 query rows per workgroup, keys split over 4 waves
         using KSplit = MfmaConfig<D, CAUSAL, 2, 4, 32>;
-        return launch_ksplit<T, KSplit>(q, k, v, o, lse, S, BH, c, stream);
+        return launch_ksplit<T, KSplit>(a);
     }
-    return launch_cfg<T, Small>(q, k, v, o, lse, S, BH, c, stream);
+    return launch_cfg<T, Small>(a);
 }
 
 template <int D, bool CAUSAL>
-int launch_f32(const void* q, const void* k, const void* v, void* o, float* lse, int S, int BH,
-               float c, hipStream_t stream) {
-    const int n_qblk = (S + F32_BM - 1) / F32_BM;
-    const int64_t grid = (int64_t)n_qblk * BH;
+int launch_f32(const Fwd& a) {
+    const int n_qblk = (a.S + F32_BM - 1) / F32_BM;
+    const int64_t grid = (int64_t)n_qblk * a.BH;
     if (grid > (int64_t)1 << 24) return FA_ERR_TOO_LARGE;
     (void)hipGetLastError();
-    hipLaunchKernelGGL((fa_fwd_f32_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(F32Cfg<D>::NT), 0, stream,
-                       (const float*)q, (const float*)k, (const float*)v, (float*)o, lse, S, BH, n_qblk,
-                       c);
+    hipLaunchKernelGGL((fa_fwd_f32_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(F32Cfg<D>::NT), 0, a.stream,
+                       (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.o, a.lse, a.S, a.BH,
+                       n_qblk, a.G, a.wl, a.wr, a.c);
     return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
 template <int D, bool CAUSAL>
-int dispatch_dtype(int dtype, const void* q, const void* k, const void* v, void* o, float* lse, int S,
-                   int BH, float c, hipStream_t stream) {
+int dispatch_dtype(int dtype, const Fwd& a) {
     switch (dtype) {
-        case FA_DTYPE_F16: return launch_mfma<F16, D, CAUSAL>(q, k, v, o, lse, S, BH, c, stream);
-        case FA_DTYPE_BF16: return launch_mfma<BF16, D, CAUSAL>(q, k, v, o, lse, S, BH, c, stream);
-        default: return launch_f32<D, CAUSAL>(q, k, v, o, lse, S, BH, c, stream);
+        case FA_DTYPE_F16: return launch_mfma<F16, D, CAUSAL>(a);
+        case FA_DTYPE_BF16: return launch_mfma<BF16, D, CAUSAL>(a);
+        default: return launch_f32<D, CAUSAL>(a);
     }
 }
 
 template <bool CAUSAL>
-int dispatch_d(int64_t D, int dtype, const void* q, const void* k, const void* v, void* o, float* lse,
-               int S, int BH, float c, hipStream_t stream) {
+int dispatch_d(int64_t D, int dtype, const Fwd& a) {
     switch (D) {
-        case 16: return dispatch_dtype<16, CAUSAL>(dtype, q, k, v, o, lse, S, BH, c, stream);
-        case 32: return dispatch_dtype<32, CAUSAL>(dtype, q, k, v, o, lse, S, BH, c, stream);
-        case 64: return dispatch_dtype<64, CAUSAL>(dtype, q, k, v, o, lse, S, BH, c, stream);
-        default: return dispatch_dtype<128, CAUSAL>(dtype, q, k, v, o, lse, S, BH, c, stream);
+        case 16: return dispatch_dtype<16, CAUSAL>(dtype, a);
+        case 32: return dispatch_dtype<32, CAUSAL>(dtype, a);
+        case 64: return dispatch_dtype<64, CAUSAL>(dtype, a);
+        default: return dispatch_dtype<128, CAUSAL>(dtype, a);
     }
 }
 
 // ------------------------------------------------------------------ backward
 
+// One backward call's device arguments and launch parameters.
+struct Bwd {
+    const void *q, *k, *v, *o, *dout;
+    const float* lse;
+    void *dq, *dk, *dv;
+    float* delta;
+    int S, BH, G, wl, wr;
+    float c, scale;
+    hipStream_t stream;
+};
+
 template <typename T, int D, bool CAUSAL>
-int launch_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
-               void* dq, void* dk, void* dv, float* delta, int S, int BH, float c, float scale,
-               hipStream_t stream) {
+int launch_bwd(const Bwd& a) {
     using Cfg = BwdConfig<D, CAUSAL, 4>;
-    const int n_blk = (S + Cfg::BM - 1) / Cfg::BM;
-    const int64_t grid = (int64_t)n_blk * BH;
+    const int n_blk = (a.S + Cfg::BM - 1) / Cfg::BM;
+    const int64_t grid = (int64_t)n_blk * a.BH;
     if (grid > (int64_t)1 << 24) return FA_ERR_TOO_LARGE;
+    const int BHkv = a.BH / a.G;
     (void)hipGetLastError();
     // dQ (and D = rowsum(dO o O) into `delta`), then dK and dV, which read D
-    hipLaunchKernelGGL((fa_bwd_dq_kernel<T, Cfg>), dim3((unsigned)grid), dim3(Cfg::NT), 0, stream,
-                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)o,
-                       (const uint16_t*)dout, lse, (uint16_t*)dq, delta, S, BH, n_blk, c, scale);
+    hipLaunchKernelGGL((fa_bwd_dq_kernel<T, Cfg>), dim3((unsigned)grid), dim3(Cfg::NT), 0, a.stream,
+                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.o,
+                       (const uint16_t*)a.dout, a.lse, (uint16_t*)a.dq, a.delta, a.S, a.BH, n_blk, a.G, a.wl, a.wr,
+                       a.c, a.scale);
     if (hipGetLastError() != hipSuccess) return FA_ERR_LAUNCH;
-    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<T, Cfg>), dim3((unsigned)grid), dim3(Cfg::NT), 0, stream,
-                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, lse,
-                       (const float*)delta, (uint16_t*)dk, (uint16_t*)dv, S, BH, n_blk, scale);
+    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<T, Cfg>), dim3((unsigned)((int64_t)n_blk * BHkv)), dim3(Cfg::NT), 0,
+                       a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                       (const uint16_t*)a.dout, a.lse, (const float*)a.delta, (uint16_t*)a.dk, (uint16_t*)a.dv, a.S,
+                       BHkv, n_blk, a.G, a.wl, a.wr, a.scale);
     return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
 template <bool CAUSAL>
-int dispatch_bwd(int64_t D, int dtype, const void* q, const void* k, const void* v, const void* o,
-                 const void* dout, const float* lse, void* dq, void* dk, void* dv, float* delta, int S, int BH,
-                 float c, float scale, hipStream_t st) {
-#define FA_BWD_CASE(DD)                                                                                   \
-    case DD:                                                                                              \
-        return dtype == FA_DTYPE_F16                                                                      \
-                   ? launch_bwd<F16, DD, CAUSAL>(q, k, v, o, dout, lse, dq, dk, dv, delta, S, BH, c, scale, st) \
-                   : launch_bwd<BF16, DD, CAUSAL>(q, k, v, o, dout, lse, dq, dk, dv, delta, S, BH, c, scale, st);
+int dispatch_bwd(int64_t D, int dtype, const Bwd& a) {
+#define FA_BWD_CASE(DD)                                                                          \
+    case DD:                                                                                     \
+        return dtype == FA_DTYPE_F16 ? launch_bwd<F16, DD, CAUSAL>(a) : launch_bwd<BF16, DD, CAUSAL>(a);
     switch (D) {
         FA_BWD_CASE(16)
         FA_BWD_CASE(32)
@@ -181,11 +210,14 @@ int dispatch_bwd(int64_t D, int dtype, const void* q, const void* k, const void*
 #undef FA_BWD_CASE
 }
 
-// Checks shared by both entry points (no HIP call).
-int check_problem(int64_t B, int64_t H, int64_t S, int64_t D, int causal, float scale) {
-    if (B < 0 || H < 0 || S < 0) return FA_ERR_SHAPE;
+// Checks shared by the entry points (no HIP call): shapes, head dim, grouped
+// heads (H a multiple of H_kv), causal flag, window bounds, scale.
+int check_problem(int64_t B, int64_t H, int64_t H_kv, int64_t S, int64_t D, int causal, int64_t wl, int64_t wr,
+                  float scale) {
+    if (B < 0 || H < 0 || S < 0 || H_kv < 0 || (H_kv == 0 ? H != 0 : H % H_kv != 0)) return FA_ERR_SHAPE;
     if (D != 16 && D != 32 && D != 64 && D != 128) return FA_ERR_HEAD_DIM;
     if (causal != 0 && causal != 1) return FA_ERR_CAUSAL;
+    if (wl < -1 || wr < -1) return FA_ERR_WINDOW;
     // finite and > 0, tested on the bits (the library is built without NaN semantics)
     uint32_t sbits;
     memcpy(&sbits, &scale, sizeof sbits);
@@ -194,85 +226,103 @@ int check_problem(int64_t B, int64_t H, int64_t S, int64_t D, int causal, float 
     return FA_OK;
 }
 
+// Index ranges shared by the entry points; H_kv > 0 here.
+int check_sizes(int64_t B, int64_t H, int64_t S, int64_t D) {
+    const int64_t kMaxInt = 2147483647;
+    if (B > kMaxInt || H > kMaxInt || B * H > kMaxInt / 2 || S > (kMaxInt >> 1)) return FA_ERR_TOO_LARGE;
+    const int64_t BH = B * H;
+    if (BH > INT64_MAX / S || BH * S > INT64_MAX / (D * 8)) return FA_ERR_TOO_LARGE;
+    return FA_OK;
+}
+
+// The window's limits clipped to the sequence: a side that reaches past S is
+// the same as no limit.
+int clip_window(int64_t w, int64_t S) { return (w < 0 || w >= S) ? -1 : (int)w; }
+
 }  // namespace
 
-extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
-                      const float* lse, void* dq, void* dk, void* dv, float* delta, int64_t B, int64_t H,
-                      int64_t S, int64_t D, int causal, float scale, int dtype, void* stream) {
+extern "C" int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                         const float* lse, void* dq, void* dk, void* dv, float* delta, int64_t B, int64_t H,
+                         int64_t H_kv, int64_t S, int64_t D, int causal, int64_t window_left,
+                         int64_t window_right, float scale, int dtype, void* stream) {
     // ---- argument checks: no HIP call before all of them pass ----------------
-    int rc = check_problem(B, H, S, D, causal, scale);
+    int rc = check_problem(B, H, H_kv, S, D, causal, window_left, window_right, scale);
     if (rc == FA_ERR_SHAPE || rc == FA_ERR_HEAD_DIM) return rc;
     if (dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
     if (rc != FA_OK) return rc;
     if (B == 0 || H == 0 || S == 0) return FA_OK;
     if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !delta) return FA_ERR_NULL_POINTER;
-    const int64_t kMaxInt = 2147483647;
-    if (B > kMaxInt || H > kMaxInt || B * H > kMaxInt / 2 || S > (kMaxInt >> 1)) return FA_ERR_TOO_LARGE;
+    if ((rc = check_sizes(B, H, S, D)) != FA_OK) return rc;
+    if (S * D * 2 > 2147483647) return FA_ERR_TOO_LARGE;
     const int64_t BH = B * H;
-    if (BH > INT64_MAX / S || BH * S > INT64_MAX / (D * 8)) return FA_ERR_TOO_LARGE;
-    if (S * D * 2 > kMaxInt) return FA_ERR_TOO_LARGE;
-    const int64_t tb = BH * S * D * 2, vb = BH * S * 4;
+    const int64_t tb = BH * S * D * 2, kvb = B * H_kv * S * D * 2, vb = BH * S * 4;
     if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)dout | (uintptr_t)dq |
          (uintptr_t)dk | (uintptr_t)dv) & 15)
         return FA_ERR_ALIGNMENT;
     if (((uintptr_t)lse | (uintptr_t)delta) & 3) return FA_ERR_ALIGNMENT;
     // every output (dq, dk, dv, delta) apart from every other buffer
     const void* outs[4] = {dq, dk, dv, delta};
-    const int64_t out_bytes[4] = {tb, tb, tb, vb};
+    const int64_t out_bytes[4] = {tb, kvb, kvb, vb};
     const void* all[10] = {q, k, v, o, dout, lse, dq, dk, dv, delta};
-    const int64_t all_bytes[10] = {tb, tb, tb, tb, tb, vb, tb, tb, tb, vb};
+    const int64_t all_bytes[10] = {tb, kvb, kvb, tb, tb, vb, tb, kvb, kvb, vb};
     for (int i = 0; i < 4; ++i)
         for (int j = 0; j < 10; ++j)
             if (j != 6 + i && overlaps(outs[i], out_bytes[i], all[j], all_bytes[j])) return FA_ERR_ALIAS;
 
-    const float c = (float)((double)scale * 1.4426950408889634);
-    hipStream_t st = (hipStream_t)stream;
-    return causal ? dispatch_bwd<true>(D, dtype, q, k, v, o, dout, lse, dq, dk, dv, delta, (int)S, (int)BH, c,
-                                       scale, st)
-                  : dispatch_bwd<false>(D, dtype, q, k, v, o, dout, lse, dq, dk, dv, delta, (int)S, (int)BH, c,
-                                        scale, st);
+    Bwd a{q, k, v, o, dout, lse, dq, dk, dv, delta, (int)S, (int)BH, (int)(H / H_kv),
+          clip_window(window_left, S), clip_window(window_right, S),
+          (float)((double)scale * 1.4426950408889634), scale, (hipStream_t)stream};
+    return causal ? dispatch_bwd<true>(D, dtype, a) : dispatch_bwd<false>(D, dtype, a);
 }
 
-extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
-                      int64_t H, int64_t S, int64_t D, int causal, float scale, int dtype,
-                      void* stream) {
+extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                      const float* lse, void* dq, void* dk, void* dv, float* delta, int64_t B, int64_t H,
+                      int64_t S, int64_t D, int causal, float scale, int dtype, void* stream) {
+    return fa_bwd_ex(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, H, S, D, causal, -1, -1, scale, dtype, stream);
+}
+
+extern "C" int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+                         int64_t H_kv, int64_t S, int64_t D, int causal, int64_t window_left, int64_t window_right,
+                         float scale, int dtype, void* stream) {
     // ---- argument checks: no HIP call before all of them pass ----------------
-    int rc = check_problem(B, H, S, D, causal, scale);
+    int rc = check_problem(B, H, H_kv, S, D, causal, window_left, window_right, scale);
     if (rc == FA_ERR_SHAPE || rc == FA_ERR_HEAD_DIM) return rc;
     if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
     if (rc != FA_OK) return rc;
     if (B == 0 || H == 0 || S == 0) return FA_OK;  // empty problem: nothing to compute
     if (!q || !k || !v || !o || !lse) return FA_ERR_NULL_POINTER;
-    // index ranges: heads*S must fit the kernels' int arithmetic, S*D per head int64
-    const int64_t kMaxInt = 2147483647;
-    if (B > kMaxInt || H > kMaxInt || B * H > kMaxInt / 2 || S > (kMaxInt >> 1)) return FA_ERR_TOO_LARGE;
-    const int64_t BH = B * H;
-    if (BH > INT64_MAX / S || BH * S > INT64_MAX / (D * 8)) return FA_ERR_TOO_LARGE;
+    if ((rc = check_sizes(B, H, S, D)) != FA_OK) return rc;
     // the matrix-core kernels address one head's K or V rows through a buffer
     // resource with a 32-bit extent: S * D * 2 bytes must stay below 2^31
-    if (dtype != FA_DTYPE_F32 && S * D * 2 > kMaxInt) return FA_ERR_TOO_LARGE;
+    if (dtype != FA_DTYPE_F32 && S * D * 2 > 2147483647) return FA_ERR_TOO_LARGE;
+    const int64_t BH = B * H;
     const int64_t tensor_bytes = BH * S * D * elem_size(dtype);
+    const int64_t kv_bytes = B * H_kv * S * D * elem_size(dtype);
     const int64_t lse_bytes = BH * S * 4;
     if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15) return FA_ERR_ALIGNMENT;
     if (((uintptr_t)lse) & 3) return FA_ERR_ALIGNMENT;
-    if (overlaps(o, tensor_bytes, q, tensor_bytes) || overlaps(o, tensor_bytes, k, tensor_bytes) ||
-        overlaps(o, tensor_bytes, v, tensor_bytes) || overlaps(o, tensor_bytes, lse, lse_bytes) ||
-        overlaps(lse, lse_bytes, q, tensor_bytes) || overlaps(lse, lse_bytes, k, tensor_bytes) ||
-        overlaps(lse, lse_bytes, v, tensor_bytes))
+    if (overlaps(o, tensor_bytes, q, tensor_bytes) || overlaps(o, tensor_bytes, k, kv_bytes) ||
+        overlaps(o, tensor_bytes, v, kv_bytes) || overlaps(o, tensor_bytes, lse, lse_bytes) ||
+        overlaps(lse, lse_bytes, q, tensor_bytes) || overlaps(lse, lse_bytes, k, kv_bytes) ||
+        overlaps(lse, lse_bytes, v, kv_bytes))
         return FA_ERR_ALIAS;
 
     // c = scale * log2(e), rounded once to fp32: scores enter exp2 as S*c - m.
-    const float c = (float)((double)scale * 1.4426950408889634);
-    hipStream_t st = (hipStream_t)stream;
-    return causal ? dispatch_d<true>(D, dtype, q, k, v, o, lse, (int)S, (int)BH, c, st)
-                  : dispatch_d<false>(D, dtype, q, k, v, o, lse, (int)S, (int)BH, c, st);
+    Fwd a{q, k, v, o, lse, (int)S, (int)BH, (int)(H / H_kv), clip_window(window_left, S),
+          clip_window(window_right, S), (float)((double)scale * 1.4426950408889634), (hipStream_t)stream};
+    return causal ? dispatch_d<true>(D, dtype, a) : dispatch_d<false>(D, dtype, a);
+}
+
+extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+                      int64_t S, int64_t D, int causal, float scale, int dtype, void* stream) {
+    return fa_fwd_ex(q, k, v, o, lse, B, H, H, S, D, causal, -1, -1, scale, dtype, stream);
 }
 
 extern "C" const char* fa_status_string(int status) {
     switch (status) {
         case FA_OK: return "ok";
         case FA_ERR_NULL_POINTER: return "a tensor pointer is NULL";
-        case FA_ERR_SHAPE: return "B, H and S must be >= 0";
+        case FA_ERR_SHAPE: return "B, H, S must be >= 0 and H a multiple of H_kv";
         case FA_ERR_HEAD_DIM: return "head dim D must be 16, 32, 64 or 128";
         case FA_ERR_DTYPE: return "dtype must be FA_DTYPE_F32, FA_DTYPE_F16 or FA_DTYPE_BF16";
         case FA_ERR_CAUSAL: return "causal must be 0 or 1";
@@ -280,7 +330,8 @@ extern "C" const char* fa_status_string(int status) {
         case FA_ERR_ALIAS: return "outputs must not overlap each other or the inputs";
         case FA_ERR_TOO_LARGE: return "problem size exceeds the kernels' index ranges";
         case FA_ERR_LAUNCH: return "the HIP runtime rejected the kernel launch";
-        case FA_ERR_ALIGNMENT: return "q, k, v, o must be 16-byte aligned and lse 4-byte aligned";
+        case FA_ERR_ALIGNMENT: return "[B,H,S,D] tensors must be 16-byte aligned, lse and delta 4-byte aligned";
+        case FA_ERR_WINDOW: return "window bounds must be >= -1 (-1: no limit on that side)";
         default: return "unknown status";
     }
 }

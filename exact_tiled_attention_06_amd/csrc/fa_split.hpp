@@ -155,7 +155,7 @@ template <typename T, typename Cfg>
 __global__ __attribute__((amdgpu_flat_work_group_size(Cfg::NT, Cfg::NT), amdgpu_waves_per_eu(Cfg::OCC, Cfg::OCC)))
 void fa_fwd_split_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                          const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE, int S,
-                         int BH, int n_qblk, float c) {
+                         int BH, int n_qblk, int G, float c) {
     using ST = SplitTile<T, Cfg>;
     constexpr int D = Cfg::D, KS = Cfg::KS, DB = Cfg::DB;
     constexpr int BN = Cfg::BN, BM = Cfg::BM, BMW = Cfg::BMW, RB = Cfg::RB;
@@ -193,9 +193,10 @@ void fa_fwd_split_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
     const int qw = q0 + wave * BMW;
 
     const int64_t head = (int64_t)bh * S * D;
+    const int64_t kvhead = (int64_t)(bh / G) * S * D;  // grouped heads: G query heads per K/V head
     const uint16_t* qh = Q + head;
-    const __amdgpu_buffer_rsrc_t krs = head_rsrc<T>(K + head, S * RB);
-    const __amdgpu_buffer_rsrc_t vrs = head_rsrc<T>(V + head, S * RB);
+    const __amdgpu_buffer_rsrc_t krs = head_rsrc<T>(K + kvhead, S * RB);
+    const __amdgpu_buffer_rsrc_t vrs = head_rsrc<T>(V + kvhead, S * RB);
     const uint32_t koff = tile_lane_offset<Cfg, false>(wave, lane);
     const uint32_t voff = tile_lane_offset<Cfg, true>(wave, lane);
 

@@ -42,7 +42,7 @@ extern "C" {
 /* ---- status codes ------------------------------------------------------- */
 #define FA_OK 0
 #define FA_ERR_NULL_POINTER 1   /* a tensor pointer is NULL for a non-empty problem */
-#define FA_ERR_SHAPE 2          /* B, H or S is negative */
+#define FA_ERR_SHAPE 2          /* B, H or S is negative, or H is not a multiple of H_kv */
 #define FA_ERR_HEAD_DIM 3       /* D is not 16, 32, 64 or 128 */
 #define FA_ERR_DTYPE 4          /* dtype is not FA_DTYPE_F32 / _F16 / _BF16 (fa_bwd: _F16 / _BF16) */
 #define FA_ERR_CAUSAL 5         /* causal is not 0 or 1 */
@@ -52,6 +52,7 @@ extern "C" {
                                    also: one head's K or V, S * D * 2 bytes, must be < 2^31) */
 #define FA_ERR_LAUNCH 9         /* the HIP runtime rejected the kernel launch */
 #define FA_ERR_ALIGNMENT 10     /* a [B,H,S,D] tensor not 16-byte aligned, or lse / delta not 4-byte aligned */
+#define FA_ERR_WINDOW 11        /* a window bound is below -1 */
 
 /* ---- element types (the dtype argument) --------------------------------- */
 #define FA_DTYPE_F32 0
@@ -136,6 +137,38 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *o, const voi
            const float *lse, void *dq, void *dk, void *dv, float *delta,
            int64_t B, int64_t H, int64_t S, int64_t D,
            int causal, float scale, int dtype, void *stream);
+
+/*
+ * fa_fwd_ex, fa_bwd_ex -- fa_fwd and fa_bwd with grouped key/value heads and a
+ * sliding window ("Inside FlashAttention", section 6.1: MQA / GQA pass K and V
+ * with fewer heads instead of replicating them; window_size = (left, right)
+ * limits each query to nearby keys, and whole blocks outside the window are
+ * skipped like the blocks above the causal diagonal).
+ *
+ *   H_kv          key/value heads: k, v (and dk, dv) are [B,H_kv,S,D]; H must
+ *                 be a multiple of H_kv, and query head h reads key/value head
+ *                 h / (H / H_kv).  H_kv = H is plain multi-head attention,
+ *                 H_kv = 1 is MQA.  The backward sums each shared head's dK and
+ *                 dV over its H / H_kv query heads.
+ *   window_left,  query i attends to keys i - window_left .. i + window_right
+ *   window_right  (and, when causal, to none past i); -1 leaves that side
+ *                 unlimited.  A bound of S or more is the same as -1.
+ *   every other argument as for fa_fwd / fa_bwd; fa_fwd(...) is
+ *   fa_fwd_ex(..., H_kv = H, ..., window_left = window_right = -1, ...), and
+ *   likewise fa_bwd.
+ *
+ * Errors: as for fa_fwd / fa_bwd, plus FA_ERR_SHAPE when H is not a multiple
+ * of H_kv and FA_ERR_WINDOW for a window bound below -1.
+ */
+int fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse,
+              int64_t B, int64_t H, int64_t H_kv, int64_t S, int64_t D,
+              int causal, int64_t window_left, int64_t window_right,
+              float scale, int dtype, void *stream);
+int fa_bwd_ex(const void *q, const void *k, const void *v, const void *o, const void *dout,
+              const float *lse, void *dq, void *dk, void *dv, float *delta,
+              int64_t B, int64_t H, int64_t H_kv, int64_t S, int64_t D,
+              int causal, int64_t window_left, int64_t window_right,
+              float scale, int dtype, void *stream);
 
 /* A static, human-readable description of a status code (never NULL). */
 const char *fa_status_string(int status);

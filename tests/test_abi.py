@@ -179,3 +179,49 @@ def test_bwd_inputs_may_alias(fa):
     # q, k, v, o, dout share storage: only outputs are checked, so this fails
     # at the null-pointer check that follows the input checks
     assert bcall(fa, k=P, v=P, o=P, dout=P, delta=0) == fa.FA_ERR_NULL_POINTER
+
+
+# ---- fa_fwd_ex / fa_bwd_ex: grouped heads and windows
+XARGS = dict(ARGS, Hkv=1, wl=-1, wr=-1)
+
+
+def xcall(fa, **over):
+    a = dict(XARGS, **over)
+    return fa.fa_fwd_ex(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Hkv"], a["S"], a["D"],
+                        a["causal"], a["wl"], a["wr"], a["scale"], a["dtype"], a["stream"])
+
+
+def xbcall(fa, **over):
+    a = dict(BARGS, Hkv=1, wl=-1, wr=-1)
+    a.update(over)
+    return fa.fa_bwd_ex(a["q"], a["k"], a["v"], a["o"], a["dout"], a["lse"], a["dq"], a["dk"], a["dv"],
+                        a["delta"], a["B"], a["H"], a["Hkv"], a["S"], a["D"], a["causal"], a["wl"], a["wr"],
+                        a["scale"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(H=6, Hkv=4), "FA_ERR_SHAPE"),       # H not a multiple of H_kv
+    (dict(Hkv=0), "FA_ERR_SHAPE"),
+    (dict(Hkv=-1), "FA_ERR_SHAPE"),
+    (dict(wl=-2), "FA_ERR_WINDOW"),
+    (dict(wr=-7), "FA_ERR_WINDOW"),
+    (dict(q=0, wl=3), "FA_ERR_NULL_POINTER"),
+    (dict(H=4, Hkv=2, o=2 * P + 8192), "FA_ERR_ALIAS"),  # o overlaps k (k is 2 heads long)
+])
+def test_ex_rejects_bad_arguments(fa, over, code):
+    assert xcall(fa, **over) == _defines()[code]
+    if "o" not in over:  # the backward's o is an input: overlapping it is no error
+        assert xbcall(fa, **over) == _defines()[code]
+
+
+def test_ex_defaults_reach_the_plain_checks(fa):
+    # H_kv = H and no window: the extended entries check exactly as the plain ones
+    for over, code in [(dict(D=48), "FA_ERR_HEAD_DIM"), (dict(scale=-1.0), "FA_ERR_SCALE"),
+                       (dict(lse=0), "FA_ERR_NULL_POINTER")]:
+        assert xcall(fa, **over) == call(fa, **over) == _defines()[code]
+    assert xbcall(fa, dtype=0) == fa.FA_ERR_DTYPE
+
+
+@pytest.mark.parametrize("over", [dict(B=0), dict(S=0)])
+def test_ex_empty_problem_is_a_no_op(fa, over):
+    assert xcall(fa, q=0, k=0, v=0, o=0, lse=0, wl=5, **over) == fa.FA_OK
