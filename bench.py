@@ -8,7 +8,10 @@ attention-forward TFLOP/s with FLOPs = 4*B*H*S^2*D, halved for causal, and its
 fraction of the MI355X dense fp16 matrix peak (2.5 PFLOP/s).
 
 Prints one JSON line.  Also reported:
-  roofline      achieved TFLOP/s of the attention kernel from HIP events around
+  roofline      (mfma_busy_pct: SQ_VALU_MFMA_BUSY_CYCLES against the kernel's
+                cycles, from the committed rocprofv3 summary while the sources
+                match)
+                achieved TFLOP/s of the attention kernel from HIP events around
                 every timed launch on the stream it runs on, against the peak;
                 `traffic` is the HBM bytes per launch measured with rocprofv3
                 FETCH_SIZE / WRITE_SIZE (scaled by a copy-kernel calibration),
@@ -61,13 +64,31 @@ def profiled_traffic(workload):
     return None
 
 
+def profiled_mfma_busy():
+    """MFMA busy % per kernel ({'fwd', 'dq', 'dkdv'}) from the committed rocprofv3
+    summary, or {} when it does not match the current kernel sources."""
+    from exact_tiled_attention_06_amd import build
+    path = os.path.join(ROOT, "profiles", "fa_f16_d64_causal_b4h16s4096_mfma_busy.txt")
+    if not os.path.exists(path):
+        return {}
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            key, sep, val = line.partition(":")
+            if sep and not line.startswith(" "):
+                kv[key.strip()] = val.strip()
+    if kv.get("source_sha256") != build.source_hash():
+        return {}
+    return {k[len("mfma_busy_pct_"):]: float(v) for k, v in kv.items() if k.startswith("mfma_busy_pct_")}
+
+
 def time_workload(fa, torch, w, causal, steps, warmup):
     import workloads
     q, k, v = (x.to("cuda:0") for x in workloads.workload_inputs(w))
     o = torch.empty_like(q)
     lse = torch.empty((w.B, w.H, w.S), dtype=torch.float32, device="cuda:0")
     for _ in range(warmup):
-        fa.forward(q, k, v, causal=causal, scale=w.scale, out=o, lse=lse)
+        fa.forward(q, k, v, causal=causal, scale=w.scale, out=o, lse=lse, window=w.window)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
@@ -76,7 +97,7 @@ def time_workload(fa, torch, w, causal, steps, warmup):
     t0 = time.perf_counter()
     for i in range(steps):
         starts[i].record(stream)
-        fa.forward(q, k, v, causal=causal, scale=w.scale, out=o, lse=lse)
+        fa.forward(q, k, v, causal=causal, scale=w.scale, out=o, lse=lse, window=w.window)
         ends[i].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -243,9 +264,13 @@ def main():
             "kernel_ms_avg": round(avg_kernel_ms, 5),
             "kernel_ms_min": round(min(kernel_ms), 5),
             "hbm_gbs_algorithmic": round(w.hbm_bytes() / (avg_kernel_ms * 1e-3) / 1e9, 1),
+            "mfma_busy_pct": None,
         },
         "cpu_baseline": None,
     }
+
+    busy = profiled_mfma_busy() if w.name == "multihead_causal" else {}
+    out["roofline"]["mfma_busy_pct"] = busy.get("fwd")
 
     if not args.no_backward and w.dtype in ("f16", "bf16"):
         bwall, bms = time_backward(fa, torch, w, causal, args.steps, args.warmup)
@@ -271,6 +296,7 @@ def main():
                 "traffic_unit": "bytes per fa_bwd call (both kernels; HBM, rocprofv3 FETCH_SIZE + WRITE_SIZE)",
                 "kernel_ms_avg": round(bavg, 5),
                 "kernel_ms_min": round(min(bms), 5),
+                "mfma_busy_pct": {"dq": busy.get("dq"), "dkdv": busy.get("dkdv")} if busy else None,
             },
             "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline_backward(w, causal),
         }
