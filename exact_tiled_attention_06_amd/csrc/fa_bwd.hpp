@@ -44,7 +44,11 @@ struct BwdConfig {
     static constexpr bool CAUSAL = CAUSAL_;
     static constexpr int KS = L::KS, DB = L::DB, RB = L::RB, TILE = L::TILE;
     static constexpr int NT = 64 * NW;
-    static constexpr int BM = 32 * NW;  // rows (queries or keys) per workgroup
+    static constexpr int BM = 32 * NW;  // keys per dK/dV workgroup
+    // dQ kernel: 32-query blocks per wave (two halve its LDS reads per MFMA;
+    // D = 128 has no registers for a second set) and queries per workgroup
+    static constexpr int QBQ = D == 128 ? 1 : 2;
+    static constexpr int BMQ = 32 * QBQ * NW;
     // D = 128 keeps two accumulators of 64 registers each in the dK/dV kernel
     static constexpr int OCC_DQ = 2;
     static constexpr int OCC_KV = D == 128 ? 1 : 2;
@@ -150,13 +154,17 @@ void fa_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict
     const int n = lane & 31;
     const int h = lane >> 5;
 
-    // heads vary fastest; causal query blocks longest first
+    // heads vary fastest; causal query blocks longest first.  A wave owns QB
+    // blocks of 32 queries (rows qw + 32a ..), so each K, V and K^T fragment
+    // read from LDS feeds QB MFMAs.
+    constexpr int QB = Cfg::QBQ;
+    constexpr int BMQ = Cfg::BMQ;
     const int wg = blockIdx.x;
     const int bh = wg % BH;
     const int rank = wg / BH;
     const int qblk = CAUSAL ? (n_blk - 1 - rank) : rank;
-    const int q0 = qblk * BM;
-    const int qw = q0 + 32 * wave;
+    const int q0 = qblk * BMQ;
+    const int qw = q0 + 32 * QB * wave;
 
     const int64_t head = (int64_t)bh * S * D;
     const int64_t kvhead = (int64_t)(bh / G) * S * D;  // grouped heads: G query heads per K/V head
@@ -168,17 +176,28 @@ void fa_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict
     // keys of query i: lo(i) .. hi(i) (causal: up to i; window: i - wl .. i + wr)
     auto lo_of = [&](int i) { return wl >= 0 ? max(0, i - wl) : 0; };
     auto hi_of = [&](int i) { return min(CAUSAL ? i : S - 1, wr >= 0 ? i + wr : S - 1); };
-    const int qlast = min(q0 + BM, S) - 1;
+    const int qlast = min(q0 + BMQ, S) - 1;
     const int tb = lo_of(q0) / 32;                 // the workgroup's key tiles [tb, te)
     const int te = hi_of(qlast) / 32 + 1;
-    const bool live = qw < S;
-    const int wlast = min(qw + 31, S - 1);
-    const int wb = live ? lo_of(qw) / 32 : te;      // this wave's tiles [wb, we)
-    const int we = live ? hi_of(wlast) / 32 + 1 : te;
-    const int ml = (lo_of(wlast) + 31) / 32;        // tiles in [ml, mu) need no mask
-    const int mu = (hi_of(qw) + 1) / 32;
-    const int qrow = min(qw + n, S - 1);
-    const int first = lo_of(qrow), last = hi_of(qrow);
+    // per block a: tiles in [ml, mu) need no mask; the wave computes tiles
+    // [wb, we), the union over its blocks (a block masks the tiles outside its
+    // own range entirely)
+    int ml[QB], mu[QB], first[QB], last[QB], qrow[QB];
+    int wb = te, we = te;
+#pragma unroll
+    for (int a = 0; a < QB; ++a) {
+        const int r0 = qw + 32 * a;
+        const int rl = min(r0 + 31, S - 1);
+        ml[a] = r0 < S ? (lo_of(rl) + 31) / 32 : te;
+        mu[a] = r0 < S ? (hi_of(r0) + 1) / 32 : 0;
+        if (r0 < S) {
+            wb = min(wb, lo_of(r0) / 32);
+            we = a == 0 ? hi_of(rl) / 32 + 1 : max(we, hi_of(rl) / 32 + 1);
+        }
+        qrow[a] = min(r0 + n, S - 1);
+        first[a] = lo_of(qrow[a]);
+        last[a] = hi_of(qrow[a]);
+    }
 
     auto stage = [&](auto par, int t) __attribute__((always_inline)) {
         constexpr int P = decltype(par)::value;
@@ -190,65 +209,79 @@ void fa_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict
     using P1 = std::integral_constant<int, 1>;
     stage(P0{}, tb);
 
-    // resident: Q and dO fragments of the wave's 32 queries; D = rowsum(dO o O)
-    u32x4 qf[KS], df[KS];
-    row_frags<KS>(Q + head, qrow, D, h, qf);
-    row_frags<KS>(dO + head, qrow, D, h, df);
-    float delta;
-    {
+    // resident: Q and dO fragments of the wave's queries; D = rowsum(dO o O)
+    u32x4 qf[QB][KS], df[QB][KS];
+    float delta[QB], lse2[QB];
+#pragma unroll
+    for (int a = 0; a < QB; ++a) {
+        row_frags<KS>(Q + head, qrow[a], D, h, qf[a]);
+        row_frags<KS>(dO + head, qrow[a], D, h, df[a]);
         u32x4 of[KS];
-        row_frags<KS>(O + head, qrow, D, h, of);
+        row_frags<KS>(O + head, qrow[a], D, h, of);
         float part = 0.f;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) part += dot8<T>(df[ks], of[ks]);
-        delta = halves_sum(part);
+        for (int ks = 0; ks < KS; ++ks) part += dot8<T>(df[a][ks], of[ks]);
+        delta[a] = halves_sum(part);
+        if (h == 0 && qw + 32 * a + n < S) DELTA[(int64_t)bh * S + qw + 32 * a + n] = delta[a];
+        lse2[a] = LSE[(int64_t)bh * S + qrow[a]] * kLog2e;
     }
-    if (h == 0 && qw + n < S) DELTA[(int64_t)bh * S + qw + n] = delta;
-    const float lse2 = LSE[(int64_t)bh * S + qrow] * kLog2e;
 
     int offk[KS], offv[DB];
     frag_offsets<L>(lane, offk, offv);
 
-    f32x16 dqacc[DB];
+    f32x16 dqacc[QB][DB];
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+    for (int a = 0; a < QB; ++a)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) dqacc[db][r] = 0.f;
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) dqacc[a][db][r] = 0.f;
 
     auto step = [&](auto par, int t) __attribute__((always_inline)) {
         constexpr int P = decltype(par)::value;
         wait_vmcnt0();
         __syncthreads();
         if (t + 1 < te) stage(std::integral_constant<int, 1 - P>{}, t + 1);
-        if (t < wb || t >= we) return;
+        if (t < wb || t >= we) return;  // wave-uniform
         const f32x16 zero = {};
-        f32x16 st = zero, dpt = zero;
+        f32x16 st[QB], dpt[QB];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            st = mfma32x32x16<T>(W::k_frag(krb[P], offk, 0, ks), qf[ks], ks == 0 ? zero : st);
-            dpt = mfma32x32x16<T>(W::k_frag(vrb[P], offk, 0, ks), df[ks], ks == 0 ? zero : dpt);
-        }
-        if (t < ml || t >= mu) {
-            // key of register r: 32t + 8(r/4) + 4h + r%4, visible iff first <= key <= last
-            const int k0 = t * 32 + 4 * h;
+            const u32x4 kfr = W::k_frag(krb[P], offk, 0, ks);
+            const u32x4 vfr = W::k_frag(vrb[P], offk, 0, ks);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int key = k0 + 8 * (r >> 2) + (r & 3);
-                if (key < first || key > last) st[r] = kNegInf;
+            for (int a = 0; a < QB; ++a) {
+                st[a] = mfma32x32x16<T>(kfr, qf[a][ks], ks == 0 ? zero : st[a]);
+                dpt[a] = mfma32x32x16<T>(vfr, df[a][ks], ks == 0 ? zero : dpt[a]);
             }
         }
-        u32x4 dsp[2];
+        u32x4 dsp[QB][2];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float p0 = exp2_fast(__builtin_fmaf(st[2 * i], c, -lse2));
-            const float p1 = exp2_fast(__builtin_fmaf(st[2 * i + 1], c, -lse2));
-            dsp[i >> 2][i & 3] = pack2<T>(p0 * (dpt[2 * i] - delta), p1 * (dpt[2 * i + 1] - delta));
+        for (int a = 0; a < QB; ++a) {
+            if (t < ml[a] || t >= mu[a]) {
+                // key of register r: 32t + 8(r/4) + 4h + r%4, visible iff first <= key <= last
+                const int k0 = t * 32 + 4 * h;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = k0 + 8 * (r >> 2) + (r & 3);
+                    if (key < first[a] || key > last[a]) st[a][r] = kNegInf;
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float p0 = exp2_fast(__builtin_fmaf(st[a][2 * i], c, -lse2[a]));
+                const float p1 = exp2_fast(__builtin_fmaf(st[a][2 * i + 1], c, -lse2[a]));
+                dsp[a][i >> 2][i & 3] = pack2<T>(p0 * (dpt[a][2 * i] - delta[a]), p1 * (dpt[a][2 * i + 1] - delta[a]));
+            }
         }
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
-            for (int db = 0; db < DB; ++db)
-                dqacc[db] = mfma32x32x16<T>(W::v_frag(ktb[P], offv, 0, j, db), dsp[j], dqacc[db]);
+            for (int db = 0; db < DB; ++db) {
+                const u32x4 ktf = W::v_frag(ktb[P], offv, 0, j, db);
+#pragma unroll
+                for (int a = 0; a < QB; ++a) dqacc[a][db] = mfma32x32x16<T>(ktf, dsp[a][j], dqacc[a][db]);
+            }
     };
     int t = tb;
     for (; t + 1 < te; t += 2) {
@@ -257,7 +290,9 @@ void fa_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict
     }
     if (t < te) step(P0{}, t);
 
-    if (qw + n < S) store_t<T, D, DB>(dQ + head, qw + n, h, dqacc, scale);
+#pragma unroll
+    for (int a = 0; a < QB; ++a)
+        if (qw + 32 * a + n < S) store_t<T, D, DB>(dQ + head, qw + 32 * a + n, h, dqacc[a], scale);
 }
 
 // ---------------------------------------------------------------- dK/dV kernel

@@ -178,16 +178,17 @@ struct Bwd {
 template <typename T, int D, bool CAUSAL>
 int launch_bwd(const Bwd& a) {
     using Cfg = BwdConfig<D, CAUSAL, 4>;
-    const int n_blk = (a.S + Cfg::BM - 1) / Cfg::BM;
+    const int n_blk = (a.S + Cfg::BM - 1) / Cfg::BM;     // key blocks (dK/dV kernel)
+    const int n_qblk = (a.S + Cfg::BMQ - 1) / Cfg::BMQ;  // query blocks (dQ kernel)
     const int64_t grid = (int64_t)n_blk * a.BH;
     if (grid > (int64_t)1 << 24) return FA_ERR_TOO_LARGE;
     const int BHkv = a.BH / a.G;
     (void)hipGetLastError();
     // dQ (and D = rowsum(dO o O) into `delta`), then dK and dV, which read D
-    hipLaunchKernelGGL((fa_bwd_dq_kernel<T, Cfg>), dim3((unsigned)grid), dim3(Cfg::NT), 0, a.stream,
-                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.o,
-                       (const uint16_t*)a.dout, a.lse, (uint16_t*)a.dq, a.delta, a.S, a.BH, n_blk, a.G, a.wl, a.wr,
-                       a.c, a.scale);
+    hipLaunchKernelGGL((fa_bwd_dq_kernel<T, Cfg>), dim3((unsigned)((int64_t)n_qblk * a.BH)), dim3(Cfg::NT), 0,
+                       a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                       (const uint16_t*)a.o, (const uint16_t*)a.dout, a.lse, (uint16_t*)a.dq, a.delta, a.S, a.BH,
+                       n_qblk, a.G, a.wl, a.wr, a.c, a.scale);
     if (hipGetLastError() != hipSuccess) return FA_ERR_LAUNCH;
     hipLaunchKernelGGL((fa_bwd_dkdv_kernel<T, Cfg>), dim3((unsigned)((int64_t)n_blk * BHkv)), dim3(Cfg::NT), 0,
                        a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
