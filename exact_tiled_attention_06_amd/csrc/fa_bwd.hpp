@@ -303,7 +303,7 @@ void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
                         const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
                         const float* __restrict__ LSE, const float* __restrict__ DELTA,
                         uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int S, int BHkv, int n_blk, int G,
-                        int wl, int wr, float scale) {
+                        int wl, int wr, float c, float scale) {
     using L = typename Cfg::L;
     using W = WaveTile<T, L>;
     constexpr int D = Cfg::D, KS = Cfg::KS, DB = Cfg::DB, RB = Cfg::RB, BM = Cfg::BM;
@@ -381,9 +381,9 @@ void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
         load_tile<T, L, true>(otb[P], ors, toff, t * 32, wave, lane);
     };
     // A tile's 32 lse and D values go through lanes 0..31 of wave 0: loaded
-    // into registers one tile ahead, written to LDS (plain stores) after the
-    // next wait, before the barrier that publishes the tile.  Rows past S get
-    // 0 and are masked.
+    // into registers one tile ahead, written to LDS (plain stores, lse times
+    // log2 e) after the next wait, before the barrier that publishes the tile.
+    // Rows past S get 0 and are masked.
     float lreg = 0.f, dreg = 0.f;
     const bool ld_lane = wave == 0 && lane < 32;
     auto fetch_ld = [&](int u) __attribute__((always_inline)) {
@@ -424,7 +424,7 @@ void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
         constexpr int P = decltype(par)::value;
         wait_vmcnt0();
         if (ld_lane) {
-            lsb[P][lane] = lreg;
+            lsb[P][lane] = lreg * kLog2e;
             dlb[P][lane] = dreg;
         }
         __syncthreads();
@@ -456,25 +456,34 @@ void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
                 dd[4 * g + e] = b[e];
             }
         }
-        // queries outside qlo .. qhi (which ends before S) do not see this
-        // lane's key: only tiles outside [ml, mu) have any
-        const bool edge = t < ml || t >= mu;
+        // P = exp2(S c - lse log2 e) and dS = P o (dP - D), packed for the
+        // MFMAs.  Queries outside qlo .. qhi (which ends before S) do not see
+        // this lane's key; only tiles outside [ml, mu) have any, so the mask
+        // is compiled into a second copy taken by a wave-uniform branch.
         u32x4 pp[2], dsp[2];
+        auto probs = [&](auto masked) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            float pv[2], dv[2];
+            for (int i = 0; i < 8; ++i) {
+                float pv[2], dv[2];
 #pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                const int r = 2 * i + e;
-                const int q = t * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                const bool hide = edge & ((q < qlo) | (q > qhi));
-                const float p = hide ? 0.f : exp2_fast(kLog2e * __builtin_fmaf(s[r], scale, -lse[r]));
-                pv[e] = p;
-                dv[e] = p * (dp[r] - dd[r]);
+                for (int e = 0; e < 2; ++e) {
+                    const int r = 2 * i + e;
+                    float p = exp2_fast(__builtin_fmaf(s[r], c, -lse[r]));
+                    if constexpr (decltype(masked)::value) {
+                        const int q = t * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                        p = ((q < qlo) | (q > qhi)) ? 0.f : p;
+                    }
+                    pv[e] = p;
+                    dv[e] = p * (dp[r] - dd[r]);
+                }
+                pp[i >> 2][i & 3] = pack2<T>(pv[0], pv[1]);
+                dsp[i >> 2][i & 3] = pack2<T>(dv[0], dv[1]);
             }
-            pp[i >> 2][i & 3] = pack2<T>(pv[0], pv[1]);
-            dsp[i >> 2][i & 3] = pack2<T>(dv[0], dv[1]);
-        }
+        };
+        if (t < ml || t >= mu)
+            probs(std::true_type{});
+        else
+            probs(std::false_type{});
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll

@@ -193,7 +193,7 @@ int launch_bwd(const Bwd& a) {
     hipLaunchKernelGGL((fa_bwd_dkdv_kernel<T, Cfg>), dim3((unsigned)((int64_t)n_blk * BHkv)), dim3(Cfg::NT), 0,
                        a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                        (const uint16_t*)a.dout, a.lse, (const float*)a.delta, (uint16_t*)a.dk, (uint16_t*)a.dv, a.S,
-                       BHkv, n_blk, a.G, a.wl, a.wr, a.scale);
+                       BHkv, n_blk, a.G, a.wl, a.wr, a.c, a.scale);
     return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
