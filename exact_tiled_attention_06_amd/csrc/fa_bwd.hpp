@@ -381,9 +381,9 @@ void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
         load_tile<T, L, true>(otb[P], ors, toff, t * 32, wave, lane);
     };
     // A tile's 32 lse and D values go through lanes 0..31 of wave 0: loaded
-    // into registers one tile ahead, written to LDS (plain stores, lse times
-    // log2 e) after the next wait, before the barrier that publishes the tile.
-    // Rows past S get 0 and are masked.
+    // into registers one tile ahead, written to LDS (plain stores: lse times
+    // log2 e, and -D) after the next wait, before the barrier that publishes
+    // the tile.  Rows past S get 0 and are masked.
     float lreg = 0.f, dreg = 0.f;
     const bool ld_lane = wave == 0 && lane < 32;
     auto fetch_ld = [&](int u) __attribute__((always_inline)) {
@@ -425,7 +425,7 @@ void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
         wait_vmcnt0();
         if (ld_lane) {
             lsb[P][lane] = lreg * kLog2e;
-            dlb[P][lane] = dreg;
+            dlb[P][lane] = -dreg;
         }
         __syncthreads();
         if (u + 1 < nsteps) {
@@ -434,16 +434,11 @@ void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
         }
         const int t = t0 + u % nt;
         if (t < tw0 || t >= tw1) return;  // wave-uniform
-        const f32x16 zero = {};
-        f32x16 s = zero, dp = zero;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            s = mfma32x32x16<T>(W::k_frag(qrb[P], offk, 0, ks), kf[ks], ks == 0 ? zero : s);
-            dp = mfma32x32x16<T>(W::k_frag(orb[P], offk, 0, ks), vf[ks], ks == 0 ? zero : dp);
-        }
-        // query of register r: 32t + 8(r/4) + 4h + r%4; lse and D for the four
-        // consecutive queries of each register group come in one 16-byte read
-        float lse[16], dd[16];
+        // query of register r: 32t + 8(r/4) + 4h + r%4; lse and -D for the
+        // four consecutive queries of each register group come in one 16-byte
+        // read.  dP starts from -D, so its accumulator ends as dP - D.
+        float lse[16];
+        f32x16 ndd;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             // (read as a float vector: a bit_cast of a vector-element lvalue
@@ -453,8 +448,15 @@ void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 lse[4 * g + e] = a[e];
-                dd[4 * g + e] = b[e];
+                ndd[4 * g + e] = b[e];
             }
+        }
+        const f32x16 zero = {};
+        f32x16 s = zero, dp = ndd;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            s = mfma32x32x16<T>(W::k_frag(qrb[P], offk, 0, ks), kf[ks], ks == 0 ? zero : s);
+            dp = mfma32x32x16<T>(W::k_frag(orb[P], offk, 0, ks), vf[ks], dp);
         }
         // P = exp2(S c - lse log2 e) and dS = P o (dP - D), packed for the
         // MFMAs.  Queries outside qlo .. qhi (which ends before S) do not see
@@ -474,7 +476,7 @@ void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
                         p = ((q < qlo) | (q > qhi)) ? 0.f : p;
                     }
                     pv[e] = p;
-                    dv[e] = p * (dp[r] - dd[r]);
+                    dv[e] = p * dp[r];
                 }
                 pp[i >> 2][i & 3] = pack2<T>(pv[0], pv[1]);
                 dsp[i >> 2][i & 3] = pack2<T>(dv[0], dv[1]);
