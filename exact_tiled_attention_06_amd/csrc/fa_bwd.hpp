@@ -77,15 +77,24 @@ __device__ __forceinline__ float dot8<BF16>(u32x4 a, u32x4 b) {
 }
 
 // Operand fragments of one row of a [S,D] head: lane (n, h) gets
-// X[row][16ks + 8h .. +7] for every k-step ks (row clamped to S-1).
+// X[row][16ks + 8h .. +7] for every k-step ks (row clamped to S-1).  The
+// loads are only issued here; pin_frags, called once every load is in flight,
+// keeps them resident.
 template <int KS>
 __device__ __forceinline__ void row_frags(const uint16_t* xh, int row, int D, int h, u32x4 (&f)[KS]) {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        f[ks] = *reinterpret_cast<const u32x4*>(xh + (int64_t)row * D + ks * 16 + h * 8);
-        pin(f[ks]);
-    }
+    for (int ks = 0; ks < KS; ++ks) f[ks] = *reinterpret_cast<const u32x4*>(xh + (int64_t)row * D + ks * 16 + h * 8);
 }
+
+template <int KS>
+__device__ __forceinline__ void pin_frags(u32x4 (&f)[KS]) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) pin(f[ks]);
+}
+
+// Compiler-only barrier: memory accesses are not moved across it, so loads
+// before it are issued before those after it.
+__device__ __forceinline__ void issue_order() { asm volatile("" ::: "memory"); }
 
 // LDS byte offsets of a lane's fragment reads (the forward's formulas): row
 // reads of chunk (2ks + h), and the transposed reads of dims 32db + ...
@@ -207,20 +216,27 @@ void fa_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict
     };
     using P0 = std::integral_constant<int, 0>;
     using P1 = std::integral_constant<int, 1>;
-    stage(P0{}, tb);
 
-    // resident: Q and dO fragments of the wave's queries; D = rowsum(dO o O)
-    u32x4 qf[QB][KS], df[QB][KS];
-    float delta[QB], lse2[QB];
+    // resident: Q and dO fragments of the wave's queries; D = rowsum(dO o O).
+    // Every fragment load is issued before the first tile's staging, and the
+    // values are waited for after it, so the two overlap.
+    u32x4 qf[QB][KS], df[QB][KS], of[QB][KS];
 #pragma unroll
     for (int a = 0; a < QB; ++a) {
         row_frags<KS>(Q + head, qrow[a], D, h, qf[a]);
         row_frags<KS>(dO + head, qrow[a], D, h, df[a]);
-        u32x4 of[KS];
-        row_frags<KS>(O + head, qrow[a], D, h, of);
+        row_frags<KS>(O + head, qrow[a], D, h, of[a]);
+    }
+    issue_order();
+    stage(P0{}, tb);
+    float delta[QB], lse2[QB];
+#pragma unroll
+    for (int a = 0; a < QB; ++a) {
+        pin_frags<KS>(qf[a]);
+        pin_frags<KS>(df[a]);
         float part = 0.f;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) part += dot8<T>(df[a][ks], of[ks]);
+        for (int ks = 0; ks < KS; ++ks) part += dot8<T>(df[a][ks], of[a][ks]);
         delta[a] = halves_sum(part);
         if (h == 0 && qw + 32 * a + n < S) DELTA[(int64_t)bh * S + qw + 32 * a + n] = delta[a];
         lse2[a] = LSE[(int64_t)bh * S + qrow[a]] * kLog2e;
@@ -311,25 +327,32 @@ void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
 
     // per Q/dO tile: Q row layout (S operand), Q transposed layout (dK^T
     // operand), dO row layout (dP operand), dO transposed layout (dV^T
-    // operand), and the tile's 32 lse and D values; two buffers each
+    // operand), and the tile's 32 lse and D values; three buffers each, so
+    // that tiles are staged two steps ahead
     __shared__ __attribute__((aligned(1024))) char qr0[Cfg::TILE];
     __shared__ __attribute__((aligned(1024))) char qr1[Cfg::TILE];
+    __shared__ __attribute__((aligned(1024))) char qr2[Cfg::TILE];
     __shared__ __attribute__((aligned(1024))) char qt0[Cfg::TILE];
     __shared__ __attribute__((aligned(1024))) char qt1[Cfg::TILE];
+    __shared__ __attribute__((aligned(1024))) char qt2[Cfg::TILE];
     __shared__ __attribute__((aligned(1024))) char or0[Cfg::TILE];
     __shared__ __attribute__((aligned(1024))) char or1[Cfg::TILE];
+    __shared__ __attribute__((aligned(1024))) char or2[Cfg::TILE];
     __shared__ __attribute__((aligned(1024))) char ot0[Cfg::TILE];
     __shared__ __attribute__((aligned(1024))) char ot1[Cfg::TILE];
+    __shared__ __attribute__((aligned(1024))) char ot2[Cfg::TILE];
     __shared__ __attribute__((aligned(16))) float ls0[32];
     __shared__ __attribute__((aligned(16))) float ls1[32];
+    __shared__ __attribute__((aligned(16))) float ls2[32];
     __shared__ __attribute__((aligned(16))) float dl0[32];
     __shared__ __attribute__((aligned(16))) float dl1[32];
-    FA_LDS char* const qrb[2] = {(FA_LDS char*)qr0, (FA_LDS char*)qr1};
-    FA_LDS char* const qtb[2] = {(FA_LDS char*)qt0, (FA_LDS char*)qt1};
-    FA_LDS char* const orb[2] = {(FA_LDS char*)or0, (FA_LDS char*)or1};
-    FA_LDS char* const otb[2] = {(FA_LDS char*)ot0, (FA_LDS char*)ot1};
-    FA_LDS float* const lsb[2] = {(FA_LDS float*)ls0, (FA_LDS float*)ls1};
-    FA_LDS float* const dlb[2] = {(FA_LDS float*)dl0, (FA_LDS float*)dl1};
+    __shared__ __attribute__((aligned(16))) float dl2[32];
+    FA_LDS char* const qrb[3] = {(FA_LDS char*)qr0, (FA_LDS char*)qr1, (FA_LDS char*)qr2};
+    FA_LDS char* const qtb[3] = {(FA_LDS char*)qt0, (FA_LDS char*)qt1, (FA_LDS char*)qt2};
+    FA_LDS char* const orb[3] = {(FA_LDS char*)or0, (FA_LDS char*)or1, (FA_LDS char*)or2};
+    FA_LDS char* const otb[3] = {(FA_LDS char*)ot0, (FA_LDS char*)ot1, (FA_LDS char*)ot2};
+    FA_LDS float* const lsb[3] = {(FA_LDS float*)ls0, (FA_LDS float*)ls1, (FA_LDS float*)ls2};
+    FA_LDS float* const dlb[3] = {(FA_LDS float*)dl0, (FA_LDS float*)dl1, (FA_LDS float*)dl2};
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -381,31 +404,53 @@ void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
         load_tile<T, L, true>(otb[P], ors, toff, t * 32, wave, lane);
     };
     // A tile's 32 lse and D values go through lanes 0..31 of wave 0: loaded
-    // into registers one tile ahead, written to LDS (plain stores: lse times
-    // log2 e, and -D) after the next wait, before the barrier that publishes
-    // the tile.  Rows past S get 0 and are masked.
-    float lreg = 0.f, dreg = 0.f;
+    // into registers (three rotating pairs) with the tile's staging, two
+    // steps ahead, and written to LDS (plain stores: lse times log2 e, and -D)
+    // before the barrier that publishes the tile.  Every lane loads, so that
+    // no branch or merge needs a loaded value early, through buffer loads
+    // (which the compiler keeps in issue order with the staging); rows past S
+    // read as 0 and occur only in tiles outside [ml, mu), where the mask sets
+    // their P to 0.
+    float lreg[3], dreg[3];
     const bool ld_lane = wave == 0 && lane < 32;
-    auto fetch_ld = [&](int u) __attribute__((always_inline)) {
+    auto fetch_ld = [&](auto par, int u) __attribute__((always_inline)) {
+        constexpr int P = decltype(par)::value;
         const int64_t qrow0 = (int64_t)(kvbh * G + u / nt) * S;
-        const int row = (t0 + u % nt) * 32 + lane;
-        if (ld_lane && row < S) {
-            lreg = LSE[qrow0 + row];
-            dreg = DELTA[qrow0 + row];
-        } else {
-            lreg = 0.f;
-            dreg = 0.f;
-        }
+        const __amdgpu_buffer_rsrc_t lrs = __builtin_amdgcn_make_buffer_rsrc((void*)(LSE + qrow0), 0, S * 4, kBufferFlags);
+        const __amdgpu_buffer_rsrc_t drs = __builtin_amdgcn_make_buffer_rsrc((void*)(DELTA + qrow0), 0, S * 4, kBufferFlags);
+        const int row = (t0 + u % nt) * 32 + n;
+        lreg[P] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(lrs, row * 4, 0, 0));
+        dreg[P] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(drs, row * 4, 0, 0));
     };
     using P0 = std::integral_constant<int, 0>;
     using P1 = std::integral_constant<int, 1>;
-    stage(P0{}, 0);
-    fetch_ld(0);
+    using P2 = std::integral_constant<int, 2>;
+    // This wave's vector-memory operations per step: the lse and D loads, and
+    // the tile transfers (spread over the first LOADS waves).  Every step
+    // issues them (steps past the last repeat the last tile into a buffer that
+    // is not read again, and the step count is padded to the unroll of 3), so
+    // the loop body is straight-line in its loads and one wait count holds.
+    constexpr int kStepOps = 2 + 4 * L::LOADS_PER_WAVE;
+    const bool stages = L::LOADS >= L::NW || wave < L::LOADS;  // wave-uniform
+    const int ulast = nsteps - 1;
 
-    // resident: K and V fragments of the wave's 32 keys
+    // resident: K and V fragments of the wave's 32 keys, loaded together with
+    // the first two steps' loads; the prologue ends with all of them complete
+    // (the loop's wait counts then hold from its first step)
     u32x4 kf[KS], vf[KS];
     row_frags<KS>(K + kvhead, krow, D, h, kf);
     row_frags<KS>(V + kvhead, krow, D, h, vf);
+    fetch_ld(P0{}, 0);
+    stage(P0{}, 0);
+    fetch_ld(P1{}, min(1, ulast));
+    stage(P1{}, min(1, ulast));
+    // (the asm operands make the compiler complete these loads here rather
+    // than sink them into the loop, where their waits would land in every
+    // iteration)
+    asm volatile("" : "+v"(lreg[0]), "+v"(dreg[0]), "+v"(lreg[1]), "+v"(dreg[1]));
+    wait_vmcnt0();
+    pin_frags<KS>(kf);
+    pin_frags<KS>(vf);
 
     int offk[KS], offv[DB];
     frag_offsets<L>(lane, offk, offv);
@@ -419,19 +464,22 @@ void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
             dvacc[db][r] = 0.f;
         }
 
-    // step u, buffers of parity u % 2
+    // step u, buffers u % 3: tile u and its lse and D were loaded two steps
+    // earlier; the loads issued last step may still be in flight
     auto step = [&](auto par, int u) __attribute__((always_inline)) {
         constexpr int P = decltype(par)::value;
-        wait_vmcnt0();
+        if (stages)
+            wait_vmcnt<kStepOps>();
+        else
+            wait_vmcnt<2>();
         if (ld_lane) {
-            lsb[P][lane] = lreg * kLog2e;
-            dlb[P][lane] = -dreg;
+            lsb[P][lane] = lreg[P] * kLog2e;
+            dlb[P][lane] = -dreg[P];
         }
-        __syncthreads();
-        if (u + 1 < nsteps) {
-            stage(std::integral_constant<int, 1 - P>{}, u + 1);
-            fetch_ld(u + 1);
-        }
+        lds_barrier();
+        fetch_ld(std::integral_constant<int, (P + 2) % 3>{}, min(u + 2, ulast));
+        stage(std::integral_constant<int, (P + 2) % 3>{}, min(u + 2, ulast));
+        if (u >= nsteps) return;  // padding step
         const int t = t0 + u % nt;
         if (t < tw0 || t >= tw1) return;  // wave-uniform
         // query of register r: 32t + 8(r/4) + 4h + r%4; lse and -D for the
@@ -494,12 +542,12 @@ void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
                 dkacc[db] = mfma32x32x16<T>(W::v_frag(qtb[P], offv, 0, j, db), dsp[j], dkacc[db]);
             }
     };
-    int u = 0;
-    for (; u + 1 < nsteps; u += 2) {
+    for (int u = 0; u < nsteps; u += 3) {
         step(P0{}, u);
         step(P1{}, u + 1);
+        step(P2{}, u + 2);
     }
-    if (u < nsteps) step(P0{}, u);
+    wait_vmcnt0();  // the spare stagings of the last steps
 
     if (live && kw + n < S) {
         store_t<T, D, DB>(dK + kvhead, kw + n, h, dkacc, scale);

@@ -116,6 +116,22 @@ __device__ __forceinline__ int swz_v(int row) {
 
 __device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Wait until at most N of this wave's vector-memory operations are
+// outstanding (they complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N <= 15, "vmcnt immediate");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+
+// Workgroup barrier that orders LDS accesses only: it waits for this wave's
+// LDS operations (lgkmcnt) but not for its vector-memory loads, so HBM -> LDS
+// transfers of later tiles stay in flight across it (__syncthreads' fence
+// waits for those too).  Data written by such a transfer is published by the
+// issuing wave's own vmcnt wait before the barrier.  The memory clobber keeps
+// the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // Wait until at most n (0..8, wave-uniform) of this wave's vector-memory
 // operations are outstanding; s_waitcnt takes the count as an immediate.
 __device__ __forceinline__ void wait_vmcnt_le(int n) {
