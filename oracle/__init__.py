@@ -13,7 +13,9 @@ section 1.1), the stable softmax with the row maximum subtracted
 ("从零训练语言模型（第二部分）", section "安全 / 在线 softmax") and the per-row
 log-sum-exp ``lse = m + ln l`` ("Inside FlashAttention", section 2.4).  Causal
 means query ``i`` sees keys ``0..i`` ("Triton 实现", the naive listing's
-upper-triangular mask).
+upper-triangular mask), in absolute positions when queries and keys differ in
+number (the CS336 write-up's forward kernel: ``Sq`` queries, ``Sk`` keys, keys
+at or past ``Sk`` absent); a row left with no key has o = 0 and lse = -inf.
 
 The gradients (``attention_bwd``) follow the backward equations of
 "从零训练语言模型（第二部分）", section "反向传播", with the softmax Jacobian's row
@@ -54,16 +56,17 @@ def _as_f64(a) -> np.ndarray:
 
 
 def _shapes(q, k, v, extra=()):
-    """[B,H,S,D] queries, [B,Hkv,S,D] keys and values (H a multiple of Hkv)."""
+    """[B,H,Sq,D] queries, [B,Hkv,Sk,D] keys and values (H a multiple of Hkv):
+    returns B, H, Hkv, Sq, Sk, D."""
     if q.ndim != 4 or k.ndim != 4 or v.shape != k.shape:
-        raise ValueError(f"q must be [B,H,S,D] and k, v one [B,Hkv,S,D] shape, got {q.shape}, {k.shape}, {v.shape}")
-    B, H, S, D = q.shape
-    if k.shape[0] != B or k.shape[2:] != (S, D) or k.shape[1] < 1 or H % k.shape[1] != 0:
+        raise ValueError(f"q must be [B,H,Sq,D] and k, v one [B,Hkv,Sk,D] shape, got {q.shape}, {k.shape}, {v.shape}")
+    B, H, Sq, D = q.shape
+    if k.shape[0] != B or k.shape[3] != D or k.shape[1] < 1 or H % k.shape[1] != 0:
         raise ValueError(f"k, v shape {k.shape} does not fit q {q.shape} (H must be a multiple of Hkv)")
     for x in extra:
         if x.shape != q.shape:
             raise ValueError(f"expected shape {q.shape}, got {x.shape}")
-    return B, H, k.shape[1], S, D
+    return B, H, k.shape[1], Sq, k.shape[2], D
 
 
 def _window(window):
@@ -77,22 +80,23 @@ class Oracle:
     """ctypes handle on one build of ``attn_oracle.c``.
 
     Keys and values may have fewer heads than the queries (grouped heads:
-    query head h reads key/value head h // (H // Hkv)); ``window = (left, right)``
-    limits query i to keys i - left .. i + right (-1: no limit on that side).
+    query head h reads key/value head h // (H // Hkv)) and another length
+    (q [B,H,Sq,D], k and v [B,Hkv,Sk,D]); ``window = (left, right)`` limits
+    query i to keys i - left .. i + right (-1: no limit on that side).
     """
 
     def __init__(self, library: str):
         lib = ctypes.CDLL(library)
         I64, I, D_ = ctypes.c_int64, ctypes.c_int, ctypes.c_double
         lib.oracle_attn_fwd_ex.restype = I
-        lib.oracle_attn_fwd_ex.argtypes = [_c_double_p] * 5 + [I64] * 5 + [I, I64, I64, D_]
+        lib.oracle_attn_fwd_ex.argtypes = [_c_double_p] * 5 + [I64] * 6 + [I, I64, I64, D_]
         lib.oracle_attn_fwd_rows_ex.restype = I
-        lib.oracle_attn_fwd_rows_ex.argtypes = [_c_double_p] * 3 + [I64] * 5 + [I, I64, I64, D_] + [
+        lib.oracle_attn_fwd_rows_ex.argtypes = [_c_double_p] * 3 + [I64] * 6 + [I, I64, I64, D_] + [
             _c_int64_p, I64, _c_double_p, _c_double_p]
         lib.oracle_attn_bwd_ex.restype = I
-        lib.oracle_attn_bwd_ex.argtypes = [_c_double_p] * 7 + [I64] * 5 + [I, I64, I64, D_]
+        lib.oracle_attn_bwd_ex.argtypes = [_c_double_p] * 7 + [I64] * 6 + [I, I64, I64, D_]
         lib.oracle_attn_bwd_rows_ex.restype = I
-        lib.oracle_attn_bwd_rows_ex.argtypes = [_c_double_p] * 4 + [I64] * 5 + [I, I64, I64, D_] + [
+        lib.oracle_attn_bwd_rows_ex.argtypes = [_c_double_p] * 4 + [I64] * 6 + [I, I64, I64, D_] + [
             _c_int64_p, I64, _c_double_p, _c_int64_p, I64, _c_double_p, _c_double_p]
         lib.oracle_num_threads.restype = I
         lib.oracle_num_threads.argtypes = []
@@ -107,56 +111,56 @@ class Oracle:
         return int(self._lib.oracle_num_threads())
 
     def attention(self, q, k, v, causal: bool, scale: float, window=None):
-        """Exact attention over all rows: returns (o [B,H,S,D], lse [B,H,S])."""
+        """Exact attention over all rows: returns (o [B,H,Sq,D], lse [B,H,Sq])."""
         q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
-        B, H, Hkv, S, D = _shapes(q, k, v)
+        B, H, Hkv, Sq, Sk, D = _shapes(q, k, v)
         wl, wr = _window(window)
         o = np.empty_like(q)
-        lse = np.empty((B, H, S), dtype=np.float64)
+        lse = np.empty((B, H, Sq), dtype=np.float64)
         rc = self._lib.oracle_attn_fwd_ex(self._ptr(q), self._ptr(k), self._ptr(v), self._ptr(o),
-                                          self._ptr(lse), B, H, Hkv, S, D, int(bool(causal)), wl, wr,
+                                          self._ptr(lse), B, H, Hkv, Sq, Sk, D, int(bool(causal)), wl, wr,
                                           float(scale))
         if rc != 0:
             raise ValueError(f"oracle_attn_fwd_ex failed with status {rc}")
         return o, lse
 
     def attention_rows(self, q, k, v, causal: bool, scale: float, rows, window=None):
-        """Exact attention for selected flat query rows ``(b*H + h)*S + i``:
+        """Exact attention for selected flat query rows ``(b*H + h)*Sq + i``:
         returns (o [n, D], lse [n]) in the order of ``rows``."""
         q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
-        B, H, Hkv, S, D = _shapes(q, k, v)
+        B, H, Hkv, Sq, Sk, D = _shapes(q, k, v)
         wl, wr = _window(window)
         rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
         n = rows.shape[0]
         o = np.empty((n, D), dtype=np.float64)
         lse = np.empty((n,), dtype=np.float64)
         rc = self._lib.oracle_attn_fwd_rows_ex(
-            self._ptr(q), self._ptr(k), self._ptr(v), B, H, Hkv, S, D, int(bool(causal)), wl, wr,
+            self._ptr(q), self._ptr(k), self._ptr(v), B, H, Hkv, Sq, Sk, D, int(bool(causal)), wl, wr,
             float(scale), rows.ctypes.data_as(_c_int64_p), n, self._ptr(o), self._ptr(lse))
         if rc != 0:
             raise ValueError(f"oracle_attn_fwd_rows_ex failed with status {rc}")
         return o, lse
 
     def attention_bwd(self, q, k, v, dout, causal: bool, scale: float, window=None):
-        """Gradients for upstream gradient ``dout`` [B,H,S,D]: returns
-        (dq [B,H,S,D], dk [B,Hkv,S,D], dv [B,Hkv,S,D])."""
+        """Gradients for upstream gradient ``dout`` [B,H,Sq,D]: returns
+        (dq [B,H,Sq,D], dk [B,Hkv,Sk,D], dv [B,Hkv,Sk,D])."""
         q, k, v, dout = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(dout)
-        B, H, Hkv, S, D = _shapes(q, k, v, (dout,))
+        B, H, Hkv, Sq, Sk, D = _shapes(q, k, v, (dout,))
         wl, wr = _window(window)
         dq, dk, dv = np.empty_like(q), np.empty_like(k), np.empty_like(k)
         rc = self._lib.oracle_attn_bwd_ex(self._ptr(q), self._ptr(k), self._ptr(v), self._ptr(dout),
                                           self._ptr(dq), self._ptr(dk), self._ptr(dv),
-                                          B, H, Hkv, S, D, int(bool(causal)), wl, wr, float(scale))
+                                          B, H, Hkv, Sq, Sk, D, int(bool(causal)), wl, wr, float(scale))
         if rc != 0:
             raise ValueError(f"oracle_attn_bwd_ex failed with status {rc}")
         return dq, dk, dv
 
     def attention_bwd_rows(self, q, k, v, dout, causal: bool, scale: float, rows, krows=None, window=None):
         """Gradients at selected positions: dQ of flat query rows ``rows``
-        ((b*H + h)*S + t) and dK, dV of flat key rows ``krows`` ((b*Hkv + hk)*S + t;
+        ((b*H + h)*Sq + t) and dK, dV of flat key rows ``krows`` ((b*Hkv + hk)*Sk + t;
         default: the same indices as ``rows``).  Returns (dq [n,D], dk [m,D], dv [m,D])."""
         q, k, v, dout = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(dout)
-        B, H, Hkv, S, D = _shapes(q, k, v, (dout,))
+        B, H, Hkv, Sq, Sk, D = _shapes(q, k, v, (dout,))
         wl, wr = _window(window)
         rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
         krows = rows if krows is None else np.ascontiguousarray(np.asarray(krows, dtype=np.int64))
@@ -164,7 +168,7 @@ class Oracle:
         dq = np.empty((n, D), dtype=np.float64)
         dk, dv = np.empty((m, D), dtype=np.float64), np.empty((m, D), dtype=np.float64)
         rc = self._lib.oracle_attn_bwd_rows_ex(
-            self._ptr(q), self._ptr(k), self._ptr(v), self._ptr(dout), B, H, Hkv, S, D,
+            self._ptr(q), self._ptr(k), self._ptr(v), self._ptr(dout), B, H, Hkv, Sq, Sk, D,
             int(bool(causal)), wl, wr, float(scale), rows.ctypes.data_as(_c_int64_p), n, self._ptr(dq),
             krows.ctypes.data_as(_c_int64_p), m, self._ptr(dk), self._ptr(dv))
         if rc != 0:

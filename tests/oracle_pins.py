@@ -535,6 +535,143 @@ def pin_ex_rows_entries(orc):
         _close(rk, dk.reshape(-1, D)[krows], 1e-13, "ex rows dK")
         _close(rv, dv.reshape(-1, D)[krows], 1e-13, "ex rows dV")
 
+# ------------------------------------------------ queries and keys of different length
+# Sq queries and Sk keys (the CS336 write-up's forward kernel: N_QUERIES and
+# N_KEYS, keys at or past N_KEYS absent, causal compares absolute positions,
+# so query i sees keys 0..min(i, Sk-1)).
+
+
+def _rect_band(Sq, Sk, causal, window=(-1, -1)):
+    wl, wr = window
+    i = np.arange(Sq)[:, None]
+    j = np.arange(Sk)[None, :]
+    m = np.ones((Sq, Sk), dtype=bool)
+    if causal:
+        m &= j <= i
+    if wl >= 0:
+        m &= j >= i - wl
+    if wr >= 0:
+        m &= j <= i + wr
+    return m
+
+
+def pin_rect_sdpa(orc):
+    """Sq != Sk against torch's float64 scaled_dot_product_attention (its causal
+    mask is the top-left lower triangle of the [Sq, Sk] score matrix) and the
+    logsumexp of the masked scores."""
+    seed = 400
+    for (B, H, Sq, Sk, D) in [(1, 2, 5, 9, 4), (2, 1, 9, 4, 3), (1, 1, 1, 6, 2), (1, 1, 6, 1, 2)]:
+        for causal in (False, True):
+            q = _rand((B, H, Sq, D), seed)
+            k, v = _rand((B, H, Sk, D), seed + 1), _rand((B, H, Sk, D), seed + 2)
+            seed += 3
+            o, lse = orc.attention(q, k, v, causal, 0.45)
+            tq, tk, tv = (torch.from_numpy(x.copy()) for x in (q, k, v))
+            ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=causal, scale=0.45)
+            _close(o, ref.numpy(), 1e-12, f"rect O {B,H,Sq,Sk,D} causal={causal}")
+            sc = (torch.matmul(tq, tk.transpose(-1, -2)) * 0.45).masked_fill(
+                ~torch.from_numpy(_rect_band(Sq, Sk, causal)), float("-inf"))
+            _close(lse, torch.logsumexp(sc, dim=-1).numpy(), 1e-12, f"rect lse {B,H,Sq,Sk,D} causal={causal}")
+
+
+def pin_rect_prefix(orc):
+    """Sq < Sk: the queries are the first Sq rows of a square problem over the same
+    keys, so O, lse and dQ equal that problem's first Sq rows."""
+    B, H, Sq, Sk, D = 2, 2, 5, 13, 3
+    qf, doutf = _rand((B, H, Sk, D), 420), _rand((B, H, Sk, D), 421)
+    k, v = _rand((B, H, Sk, D), 422), _rand((B, H, Sk, D), 423)
+    for causal in (False, True):
+        o1, l1 = orc.attention(qf[:, :, :Sq], k, v, causal, 0.7)
+        o2, l2 = orc.attention(qf, k, v, causal, 0.7)
+        _close(o1, o2[:, :, :Sq], 1e-15, f"rect prefix O causal={causal}")
+        _close(l1, l2[:, :, :Sq], 1e-15, f"rect prefix lse causal={causal}")
+        dq1 = orc.attention_bwd(qf[:, :, :Sq], k, v, doutf[:, :, :Sq], causal, 0.7)[0]
+        dq2 = orc.attention_bwd(qf, k, v, doutf, causal, 0.7)[0]
+        _close(dq1, dq2[:, :, :Sq], 1e-14, f"rect prefix dQ causal={causal}")
+
+
+def pin_rect_rows_past_keys(orc):
+    """Sq > Sk, causal: rows i >= Sk - 1 see every key (they equal the non-causal
+    rows) and rows i < Sk are the square causal problem on the first Sk queries."""
+    B, H, Sq, Sk, D = 1, 3, 11, 4, 5
+    q = _rand((B, H, Sq, D), 430)
+    k, v = _rand((B, H, Sk, D), 431), _rand((B, H, Sk, D), 432)
+    oc, lc = orc.attention(q, k, v, True, 0.8)
+    on, ln = orc.attention(q, k, v, False, 0.8)
+    _close(oc[:, :, Sk - 1:], on[:, :, Sk - 1:], 1e-15, "causal rows past the keys O")
+    _close(lc[:, :, Sk - 1:], ln[:, :, Sk - 1:], 1e-15, "causal rows past the keys lse")
+    os_, ls_ = orc.attention(q[:, :, :Sk], k, v, True, 0.8)
+    _close(oc[:, :, :Sk], os_, 1e-15, "causal rows below Sk O")
+    _close(lc[:, :, :Sk], ls_, 1e-15, "causal rows below Sk lse")
+
+
+def pin_rect_empty_rows(orc):
+    """A window can leave a query with no key when Sq > Sk: such a row has O = 0,
+    lse = -inf, dQ = 0 and adds nothing to dK, dV (the gradients equal those of
+    the problem without those rows)."""
+    B, H, Sq, Sk, D = 1, 2, 7, 3, 2
+    q, dout = _rand((B, H, Sq, D), 440), _rand((B, H, Sq, D), 441)
+    k, v = _rand((B, H, Sk, D), 442), _rand((B, H, Sk, D), 443)
+    for causal in (False, True):
+        window = (1, 0)  # rows 4..6 see keys i-1..i, all past Sk - 1 = 2
+        o, lse = orc.attention(q, k, v, causal, 0.6, window)
+        _close(o[:, :, 4:], np.zeros((B, H, 3, D)), 0.0, f"empty rows O causal={causal}")
+        assert np.all(np.isneginf(lse[:, :, 4:])), f"empty rows lse must be -inf, got {lse[:, :, 4:]}"
+        assert np.all(np.isfinite(lse[:, :, :4])), "rows with keys must have finite lse"
+        dq, dk, dv = orc.attention_bwd(q, k, v, dout, causal, 0.6, window)
+        _close(dq[:, :, 4:], np.zeros((B, H, 3, D)), 0.0, f"empty rows dQ causal={causal}")
+        dq4, dk4, dv4 = orc.attention_bwd(q[:, :, :4], k, v, dout[:, :, :4], causal, 0.6, window)
+        _close(dq[:, :, :4], dq4, 1e-15, "rows with keys dQ")
+        _close(dk, dk4, 1e-15, "empty rows add nothing to dK")
+        _close(dv, dv4, 1e-15, "empty rows add nothing to dV")
+
+
+def pin_rect_bwd_torch_autograd(orc):
+    """Sq != Sk gradients (with grouped heads and a window) against torch float64
+    autograd of softmax over the masked [Sq, Sk] score matrix."""
+    seed = 450
+    cases = [(1, 2, 2, 5, 9, 3, False, (-1, -1)), (1, 2, 1, 9, 5, 2, True, (-1, -1)),
+             (2, 4, 2, 6, 11, 2, True, (2, -1)), (1, 2, 2, 10, 7, 3, False, (3, 1))]
+    for (B, H, Hkv, Sq, Sk, D, causal, window) in cases:
+        q, dout = _rand((B, H, Sq, D), seed), _rand((B, H, Sq, D), seed + 1)
+        k, v = _rand((B, Hkv, Sk, D), seed + 2), _rand((B, Hkv, Sk, D), seed + 3)
+        seed += 4
+        tq = torch.from_numpy(q.copy()).requires_grad_(True)
+        tk = torch.from_numpy(k.copy()).requires_grad_(True)
+        tv = torch.from_numpy(v.copy()).requires_grad_(True)
+        ke = tk.repeat_interleave(H // Hkv, dim=1)
+        ve = tv.repeat_interleave(H // Hkv, dim=1)
+        sc = (torch.matmul(tq, ke.transpose(-1, -2)) * 0.5).masked_fill(
+            ~torch.from_numpy(_rect_band(Sq, Sk, causal, window)), float("-inf"))
+        ref_o = torch.matmul(torch.softmax(sc, dim=-1), ve)
+        o, lse = orc.attention(q, k, v, causal, 0.5, window)
+        _close(o, ref_o.detach().numpy(), 1e-12, f"rect O {Sq, Sk} causal={causal} window={window}")
+        ref_o.backward(torch.from_numpy(dout))
+        dq, dk, dv = orc.attention_bwd(q, k, v, dout, causal, 0.5, window)
+        for nm, got, ref in (("dQ", dq, tq.grad), ("dK", dk, tk.grad), ("dV", dv, tv.grad)):
+            _close(got, ref.numpy(), 1e-12, f"rect {nm} {Sq, Sk} causal={causal} window={window}")
+
+
+def pin_rect_rows_entries(orc):
+    """With Sq != Sk the row entries index query rows by Sq and key rows by Sk and
+    return exactly the full entries' rows."""
+    B, H, Hkv, Sq, Sk, D = 2, 2, 1, 6, 10, 3
+    q, dout = _rand((B, H, Sq, D), 470), _rand((B, H, Sq, D), 471)
+    k, v = _rand((B, Hkv, Sk, D), 472), _rand((B, Hkv, Sk, D), 473)
+    for causal, window in ((False, (-1, -1)), (True, (-1, -1)), (False, (2, 3))):
+        o, lse = orc.attention(q, k, v, causal, 0.4, window)
+        rows = np.array([0, 5, 6, 13, B * H * Sq - 1], dtype=np.int64)
+        ro, rl = orc.attention_rows(q, k, v, causal, 0.4, rows, window)
+        _close(ro, o.reshape(-1, D)[rows], 0.0, "rect rows entry O")
+        _close(rl, lse.reshape(-1)[rows], 0.0, "rect rows entry lse")
+        dq, dk, dv = orc.attention_bwd(q, k, v, dout, causal, 0.4, window)
+        krows = np.array([0, 9, 10, 17, B * Hkv * Sk - 1], dtype=np.int64)
+        rq, rk, rv = orc.attention_bwd_rows(q, k, v, dout, causal, 0.4, rows, krows, window)
+        _close(rq, dq.reshape(-1, D)[rows], 1e-13, "rect rows entry dQ")
+        _close(rk, dk.reshape(-1, D)[krows], 1e-13, "rect rows entry dK")
+        _close(rv, dv.reshape(-1, D)[krows], 1e-13, "rect rows entry dV")
+
+
 ALL_PINS = [
     pin_worked_example,
     pin_normalisation,
@@ -563,4 +700,10 @@ ALL_PINS = [
     pin_window_reversal,
     pin_window_finite_differences,
     pin_ex_rows_entries,
+    pin_rect_sdpa,
+    pin_rect_prefix,
+    pin_rect_rows_past_keys,
+    pin_rect_empty_rows,
+    pin_rect_bwd_torch_autograd,
+    pin_rect_rows_entries,
 ]

@@ -22,16 +22,17 @@ MUTANTS = {
     "no_normalisation": ("o_i[d] = acc[d] / l;", "o_i[d] = acc[d];"),
     "lse_base2": ("*lse_i = m + log(l);", "*lse_i = m + log2(l);"),
     "lse_drops_max": ("*lse_i = m + log(l);", "*lse_i = log(l);"),
-    "causal_off_by_one": ("int64_t a = 0, b = causal ? i : S - 1;",
-                          "int64_t a = 0, b = causal ? (i > 0 ? i - 1 : 0) : S - 1;"),
-    "causal_wrong_triangle": ("int64_t a = 0, b = causal ? i : S - 1;", "int64_t a = causal ? i : 0, b = S - 1;"),
+    "causal_off_by_one": ("int64_t a = 0, b = causal && i < Sk - 1 ? i : Sk - 1;",
+                          "int64_t a = 0, b = causal && i < Sk - 1 ? (i > 0 ? i - 1 : 0) : Sk - 1;"),
+    "causal_wrong_triangle": ("int64_t a = 0, b = causal && i < Sk - 1 ? i : Sk - 1;",
+                              "int64_t a = causal && i < Sk - 1 ? i : 0, b = Sk - 1;"),
     "k_transposed": ("const double *k_j = k_bh + j * D;", "const double *k_j = k_bh + j;"),
     "v_transposed": ("const double *v_j = v_bh + j * D;", "const double *v_j = v_bh + j;"),
-    "k_head_offset_dropped": ("k + (kvh * S + lo) * D", "k + lo * D"),
-    "v_head_offset_dropped": ("v + (kvh * S + lo) * D", "v + lo * D"),
+    "k_head_offset_dropped": ("k + (kvh * Sk + lo) * D", "k + lo * D"),
+    "v_head_offset_dropped": ("v + (kvh * Sk + lo) * D", "v + lo * D"),
     "acc_init_one": ("acc[d] = 0.0;", "acc[d] = 1.0;"),
     "l_init_one": ("double l = 0.0;", "double l = 1.0;"),
-    "q_row_offset": ("q + flat * D", "q + bh * S * D"),
+    "q_row_offset": ("q + flat * D", "q + bh * Sq * D"),
     # backward
     "bwd_drops_row_term": ("const double ds = w[j] * (g[j] - row);", "const double ds = w[j] * g[j];"),
     "bwd_ds_without_p": ("const double ds = w[j] * (g[j] - row);", "const double ds = g[j] - row;"),
@@ -43,8 +44,8 @@ MUTANTS = {
     "bwd_dv_wrong_index": ("dv_j[d] += w[j] * do_i[d];", "dv_j[d] += w[j] * do_i[0];"),
     "bwd_dp_wrong_row": ("const double *vr = v_bh + j * D;", "const double *vr = v_bh;"),
     "bwd_unnormalised_p": ("w[j] /= total;", "w[j] /= 1.0;"),
-    "bwd_causal_sees_all": ("key_range(i, S, causal, wl, wr, &lo, &hi);\n            const int64_t n_keys = hi - lo + 1;\n            const double *q_i = q_g",
-                            "key_range(i, S, 0, wl, wr, &lo, &hi);\n            const int64_t n_keys = hi - lo + 1;\n            const double *q_i = q_g"),
+    "bwd_causal_sees_all": ("key_range(i, Sk, causal, wl, wr, &lo, &hi);\n            const int64_t n_keys = hi - lo + 1;\n            const double *q_i = q_g",
+                            "key_range(i, Sk, 0, wl, wr, &lo, &hi);\n            const int64_t n_keys = hi - lo + 1;\n            const double *q_i = q_g"),
     "bwd_rows_p_not_normalised": ("const double p = exp(scale * acc - top[x]) / sum[x];",
                                   "const double p = exp(scale * acc - top[x]);"),
     "bwd_rows_key_range": ("if (t < lo || t > hi)", "if (t < lo)"),
@@ -55,8 +56,16 @@ MUTANTS = {
                                "if (wl >= 0 && i - wl + 1 > a)\n        a = i - wl + 1;"),
     "window_right_ignored": ("if (wr >= 0 && i + wr < b)\n        b = i + wr;", ""),
     "window_sides_swapped": ("if (wl >= 0 && i - wl > a)", "if (wr >= 0 && i - wr > a)"),
-    "bwd_group_not_summed": ("for (int64_t hq = 0; hq < G; ++hq) {\n        for (int64_t i = 0; i < S; ++i) {",
-                             "for (int64_t hq = G - 1; hq < G; ++hq) {\n        for (int64_t i = 0; i < S; ++i) {"),
+    "bwd_group_not_summed": ("for (int64_t hq = 0; hq < G; ++hq) {\n        for (int64_t i = 0; i < Sq; ++i) {",
+                             "for (int64_t hq = G - 1; hq < G; ++hq) {\n        for (int64_t i = 0; i < Sq; ++i) {"),
+    # queries and keys of different length
+    "empty_row_lse_zero": ("*lse_i = -INFINITY;", "*lse_i = 0.0;"),
+    "empty_row_o_one": ("o_i[d] = 0.0;\n        *lse_i = -INFINITY;", "o_i[d] = 1.0;\n        *lse_i = -INFINITY;"),
+    "causal_clip_to_first_key": ("? i : Sk - 1;", "? i : 0;"),
+    "rows_query_index_mod_sk": ("const int64_t bh = flat / Sq;\n            const int64_t i = flat % Sq;",
+                                "const int64_t bh = flat / Sq;\n            const int64_t i = flat % Sk;"),
+    "bwd_rows_query_index_mod_sk": ("const int64_t bh = qrows[r] / Sq, t = qrows[r] % Sq;",
+                                    "const int64_t bh = qrows[r] / Sq, t = qrows[r] % Sk;"),
 }
 
 
