@@ -14,11 +14,13 @@ import this package before the library exists.
     fa_status_string(status)
         the C status description;
     forward(q, k, v, causal=False, scale=None, window=None) -> (o, lse)
-        convenience on torch tensors [B,H,S,D]: allocates o (input dtype) and
-        lse (float32 [B,H,S]) and calls fa_fwd on the current stream.  The
-        default scale is 1/sqrt(D) ("T5 讲解：FlashAttention forward", section ⑥).
+        convenience on torch tensors q [B,H,S_q,D], k and v [B,H_kv,S_k,D]:
+        allocates o (input dtype) and lse (float32 [B,H,S_q]) and calls
+        fa_fwd_ex on the current stream.  The default scale is 1/sqrt(D)
+        ("T5 讲解：FlashAttention forward", section ⑥).
     fa_fwd_ex / fa_bwd_ex(...)
-        the C entry points with grouped K/V heads (H_kv) and a sliding window;
+        the C entry points with grouped K/V heads (H_kv), separate query and
+        key lengths (S_q, S_k) and a sliding window;
     backward(q, k, v, o, lse, dout, causal=False, scale=None, window=None) -> (dq, dk, dv)
         gradients for the upstream gradient dout, from the forward's o and lse;
         allocates the outputs and the D workspace and calls fa_bwd.
@@ -72,9 +74,9 @@ def _load() -> ctypes.CDLL:
         ctypes.c_int, ctypes.c_float, ctypes.c_int, ctypes.c_void_p]
     I64, I, F, P = ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_void_p
     lib.fa_fwd_ex.restype = I
-    lib.fa_fwd_ex.argtypes = [P] * 5 + [I64] * 5 + [I, I64, I64, F, I, P]
+    lib.fa_fwd_ex.argtypes = [P] * 5 + [I64] * 6 + [I, I64, I64, F, I, P]
     lib.fa_bwd_ex.restype = I
-    lib.fa_bwd_ex.argtypes = [P] * 10 + [I64] * 5 + [I, I64, I64, F, I, P]
+    lib.fa_bwd_ex.argtypes = [P] * 10 + [I64] * 6 + [I, I64, I64, F, I, P]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_status_string.argtypes = [ctypes.c_int]
     return lib
@@ -121,19 +123,23 @@ def fa_bwd(q: int, k: int, v: int, o: int, dout: int, lse: int, dq: int, dk: int
                                 float(scale), int(dtype), stream))
 
 
-def fa_fwd_ex(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, H_kv: int, S: int, D: int,
-              causal: int, window_left: int, window_right: int, scale: float, dtype: int, stream: int) -> int:
-    """The C forward with grouped K/V heads and a sliding window; returns the status code."""
-    return int(library().fa_fwd_ex(q, k, v, o, lse, B, H, H_kv, S, D, int(causal), int(window_left),
+def fa_fwd_ex(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, H_kv: int, S_q: int, S_k: int,
+              D: int, causal: int, window_left: int, window_right: int, scale: float, dtype: int,
+              stream: int) -> int:
+    """The C forward with grouped K/V heads, query and key lengths S_q, S_k and a
+    sliding window; returns the status code."""
+    return int(library().fa_fwd_ex(q, k, v, o, lse, B, H, H_kv, S_q, S_k, D, int(causal), int(window_left),
                                    int(window_right), float(scale), int(dtype), stream))
 
 
 def fa_bwd_ex(q: int, k: int, v: int, o: int, dout: int, lse: int, dq: int, dk: int, dv: int, delta: int,
-              B: int, H: int, H_kv: int, S: int, D: int, causal: int, window_left: int, window_right: int,
-              scale: float, dtype: int, stream: int) -> int:
-    """The C backward with grouped K/V heads and a sliding window; returns the status code."""
-    return int(library().fa_bwd_ex(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, H_kv, S, D, int(causal),
-                                   int(window_left), int(window_right), float(scale), int(dtype), stream))
+              B: int, H: int, H_kv: int, S_q: int, S_k: int, D: int, causal: int, window_left: int,
+              window_right: int, scale: float, dtype: int, stream: int) -> int:
+    """The C backward with grouped K/V heads, query and key lengths S_q, S_k and a
+    sliding window; returns the status code."""
+    return int(library().fa_bwd_ex(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, H_kv, S_q, S_k, D,
+                                   int(causal), int(window_left), int(window_right), float(scale), int(dtype),
+                                   stream))
 
 
 def _window(window):
@@ -144,7 +150,8 @@ def _window(window):
 
 
 def _kv_shape_ok(q: torch.Tensor, k: torch.Tensor) -> bool:
-    if k.dim() != 4 or k.shape[0] != q.shape[0] or k.shape[2:] != q.shape[2:]:
+    """k is [B,H_kv,S_k,D] for q [B,H,S_q,D]: same B and D, H a multiple of H_kv."""
+    if k.dim() != 4 or k.shape[0] != q.shape[0] or k.shape[3] != q.shape[3]:
         return False
     hq, hk = q.shape[1], k.shape[1]
     return (hq == 0 and hk == 0) or (hk >= 1 and hq % hk == 0)
@@ -161,13 +168,15 @@ def check(status: int) -> None:
 def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
             scale: float | None = None, out: torch.Tensor | None = None,
             lse: torch.Tensor | None = None, window=None):
-    """Attention forward on device tensors q [B,H,S,D], k and v [B,H_kv,S,D]
-    (H a multiple of H_kv); returns (o, lse).  ``window = (left, right)`` limits
-    query i to keys i - left .. i + right (-1: unlimited side)."""
+    """Attention forward on device tensors q [B,H,S_q,D], k and v [B,H_kv,S_k,D]
+    (H a multiple of H_kv); returns (o [B,H,S_q,D], lse [B,H,S_q]).  Causal means
+    query i sees keys 0..i; ``window = (left, right)`` limits query i to keys
+    i - left .. i + right (-1: unlimited side).  A row left with no key gets
+    o = 0 and lse = -inf."""
     if q.dim() != 4:
-        raise ValueError(f"q must be [B,H,S,D], got shape {tuple(q.shape)}")
+        raise ValueError(f"q must be [B,H,S_q,D], got shape {tuple(q.shape)}")
     if not _kv_shape_ok(q, k) or v.shape != k.shape:
-        raise ValueError(f"k, v must share a [B,H_kv,S,D] shape with H a multiple of H_kv: "
+        raise ValueError(f"k, v must share a [B,H_kv,S_k,D] shape with q's B and D and H a multiple of H_kv: "
                          f"{tuple(q.shape)}, {tuple(k.shape)}, {tuple(v.shape)}")
     if not (q.dtype == k.dtype == v.dtype) or q.dtype not in DTYPE_CODES:
         raise ValueError(f"q, k, v must share one of {list(DTYPE_CODES)}; got {q.dtype}, {k.dtype}, {v.dtype}")
@@ -176,6 +185,7 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = Fa
     if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
         raise ValueError("q, k, v must be contiguous")
     B, H, S, D = q.shape
+    S_k = k.shape[2]
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     scale = float(torch.tensor(scale, dtype=torch.float32))
@@ -190,7 +200,8 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = Fa
     stream = torch.cuda.current_stream(q.device).cuda_stream
     wl, wr = _window(window)
     status = fa_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                       B, H, k.shape[1], S, D, int(bool(causal)), wl, wr, scale, DTYPE_CODES[q.dtype], stream)
+                       B, H, k.shape[1], S, S_k, D, int(bool(causal)), wl, wr, scale, DTYPE_CODES[q.dtype],
+                       stream)
     check(status)
     return out, lse
 
@@ -199,12 +210,12 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
              dout: torch.Tensor, causal: bool = False, scale: float | None = None, window=None):
     """Attention backward (fp16 / bf16): returns (dq, dk, dv), dk and dv shaped like k.
 
-    q, o, dout are [B,H,S,D], k and v [B,H_kv,S,D]; o and lse are the forward's
-    outputs for the same q, k, v, causal, scale and window; the
+    q, o, dout are [B,H,S_q,D], k and v [B,H_kv,S_k,D]; o and lse are the
+    forward's outputs for the same q, k, v, causal, scale and window; the
     D = rowsum(dout * o) workspace is allocated here."""
     ts = (q, k, v, o, dout)
     if q.dim() != 4 or o.shape != q.shape or dout.shape != q.shape or not _kv_shape_ok(q, k) or v.shape != k.shape:
-        raise ValueError("q, o, dout must share one [B,H,S,D] shape and k, v one [B,H_kv,S,D] shape")
+        raise ValueError("q, o, dout must share one [B,H,S_q,D] shape and k, v one [B,H_kv,S_k,D] shape")
     if any(t.dtype != q.dtype for t in ts) or q.dtype not in (torch.float16, torch.bfloat16):
         raise ValueError("q, k, v, o, dout must share dtype float16 or bfloat16")
     if not all(t.is_cuda for t in ts + (lse,)):
@@ -222,7 +233,7 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
     stream = torch.cuda.current_stream(q.device).cuda_stream
     wl, wr = _window(window)
     status = fa_bwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
-                       dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), B, H, k.shape[1], S, D,
-                       int(bool(causal)), wl, wr, scale, DTYPE_CODES[q.dtype], stream)
+                       dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), B, H, k.shape[1], S,
+                       k.shape[2], D, int(bool(causal)), wl, wr, scale, DTYPE_CODES[q.dtype], stream)
     check(status)
     return dq, dk, dv

@@ -138,11 +138,11 @@ __global__ __attribute__((amdgpu_flat_work_group_size(Cfg::NT, Cfg::NT), amdgpu_
 void fa_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                       const uint16_t* __restrict__ V, const uint16_t* __restrict__ O,
                       const uint16_t* __restrict__ dO, const float* __restrict__ LSE,
-                      uint16_t* __restrict__ dQ, float* __restrict__ DELTA, int S, int BH, int n_blk, int G,
+                      uint16_t* __restrict__ dQ, float* __restrict__ DELTA, int Sq, int Sk, int BH, int n_blk, int G,
                       int wl, int wr, float c, float scale) {
     using L = typename Cfg::L;
     using W = WaveTile<T, L>;
-    constexpr int D = Cfg::D, KS = Cfg::KS, DB = Cfg::DB, RB = Cfg::RB, BM = Cfg::BM;
+    constexpr int D = Cfg::D, KS = Cfg::KS, DB = Cfg::DB, RB = Cfg::RB;
     constexpr bool CAUSAL = Cfg::CAUSAL;
 
     // per K/V tile: K row layout (S^T operand), K transposed layout (dQ^T
@@ -175,17 +175,17 @@ void fa_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict
     const int q0 = qblk * BMQ;
     const int qw = q0 + 32 * QB * wave;
 
-    const int64_t head = (int64_t)bh * S * D;
-    const int64_t kvhead = (int64_t)(bh / G) * S * D;  // grouped heads: G query heads per K/V head
-    const __amdgpu_buffer_rsrc_t krs = head_rsrc<T>(K + kvhead, S * RB);
-    const __amdgpu_buffer_rsrc_t vrs = head_rsrc<T>(V + kvhead, S * RB);
+    const int64_t head = (int64_t)bh * Sq * D;
+    const int64_t kvhead = (int64_t)(bh / G) * Sk * D;  // grouped heads: G query heads per K/V head
+    const __amdgpu_buffer_rsrc_t krs = head_rsrc<T>(K + kvhead, Sk * RB);
+    const __amdgpu_buffer_rsrc_t vrs = head_rsrc<T>(V + kvhead, Sk * RB);
     const uint32_t roff = tile_lane_offset<L, false>(wave, lane);
     const uint32_t toff = tile_lane_offset<L, true>(wave, lane);
 
     // keys of query i: lo(i) .. hi(i) (causal: up to i; window: i - wl .. i + wr)
     auto lo_of = [&](int i) { return wl >= 0 ? max(0, i - wl) : 0; };
-    auto hi_of = [&](int i) { return min(CAUSAL ? i : S - 1, wr >= 0 ? i + wr : S - 1); };
-    const int qlast = min(q0 + BMQ, S) - 1;
+    auto hi_of = [&](int i) { return min(min(CAUSAL ? i : Sk - 1, wr >= 0 ? i + wr : Sk - 1), Sk - 1); };
+    const int qlast = min(q0 + BMQ, Sq) - 1;
     const int tb = lo_of(q0) / 32;                 // the workgroup's key tiles [tb, te)
     const int te = hi_of(qlast) / 32 + 1;
     // per block a: tiles in [ml, mu) need no mask; the wave computes tiles
@@ -196,14 +196,14 @@ void fa_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict
 #pragma unroll
     for (int a = 0; a < QB; ++a) {
         const int r0 = qw + 32 * a;
-        const int rl = min(r0 + 31, S - 1);
-        ml[a] = r0 < S ? (lo_of(rl) + 31) / 32 : te;
-        mu[a] = r0 < S ? (hi_of(r0) + 1) / 32 : 0;
-        if (r0 < S) {
+        const int rl = min(r0 + 31, Sq - 1);
+        ml[a] = r0 < Sq ? (lo_of(rl) + 31) / 32 : te;
+        mu[a] = r0 < Sq ? (hi_of(r0) + 1) / 32 : 0;
+        if (r0 < Sq) {
             wb = min(wb, lo_of(r0) / 32);
             we = a == 0 ? hi_of(rl) / 32 + 1 : max(we, hi_of(rl) / 32 + 1);
         }
-        qrow[a] = min(r0 + n, S - 1);
+        qrow[a] = min(r0 + n, Sq - 1);
         first[a] = lo_of(qrow[a]);
         last[a] = hi_of(qrow[a]);
     }
@@ -238,8 +238,10 @@ void fa_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) part += dot8<T>(df[a][ks], of[a][ks]);
         delta[a] = halves_sum(part);
-        if (h == 0 && qw + 32 * a + n < S) DELTA[(int64_t)bh * S + qw + 32 * a + n] = delta[a];
-        lse2[a] = LSE[(int64_t)bh * S + qrow[a]] * kLog2e;
+        if (h == 0 && qw + 32 * a + n < Sq) DELTA[(int64_t)bh * Sq + qw + 32 * a + n] = delta[a];
+        // a row with no key (lse = -inf; all its scores are masked to -inf)
+        // takes +inf, so that its masked scores give exp2(-inf) = 0
+        lse2[a] = first[a] <= last[a] ? LSE[(int64_t)bh * Sq + qrow[a]] * kLog2e : __builtin_inff();
     }
 
     int offk[KS], offv[DB];
@@ -308,7 +310,7 @@ void fa_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict
 
 #pragma unroll
     for (int a = 0; a < QB; ++a)
-        if (qw + 32 * a + n < S) store_t<T, D, DB>(dQ + head, qw + 32 * a + n, h, dqacc[a], scale);
+        if (qw + 32 * a + n < Sq) store_t<T, D, DB>(dQ + head, qw + 32 * a + n, h, dqacc[a], scale);
 }
 
 // ---------------------------------------------------------------- dK/dV kernel
@@ -318,7 +320,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(Cfg::NT, Cfg::NT), amdgpu_
 void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                         const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
                         const float* __restrict__ LSE, const float* __restrict__ DELTA,
-                        uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int S, int BHkv, int n_blk, int G,
+                        uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int Sq, int Sk, int BHkv, int n_blk, int G,
                         int wl, int wr, float c, float scale) {
     using L = typename Cfg::L;
     using W = WaveTile<T, L>;
@@ -370,34 +372,48 @@ void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
     const int k0 = kblk * BM;
     const int kw = k0 + 32 * wave;
 
-    const int64_t kvhead = (int64_t)kvbh * S * D;
+    const int64_t kvhead = (int64_t)kvbh * Sk * D;
     const uint32_t roff = tile_lane_offset<L, false>(wave, lane);
     const uint32_t toff = tile_lane_offset<L, true>(wave, lane);
 
     // queries that see key j: ilo(j) .. ihi(j) (causal: from j; window: j - wr .. j + wl)
     auto ilo_of = [&](int j) { return max(CAUSAL ? j : 0, wr >= 0 ? j - wr : 0); };
-    auto ihi_of = [&](int j) { return min(S - 1, wl >= 0 ? j + wl : S - 1); };
-    const int klast = min(k0 + BM, S) - 1;
+    auto ihi_of = [&](int j) { return min(Sq - 1, wl >= 0 ? j + wl : Sq - 1); };
+    const int klast = min(k0 + BM, Sk) - 1;
     const int t0 = ilo_of(k0) / 32;                  // query tiles [t0, t1) of each head
     const int t1 = ihi_of(klast) / 32 + 1;
     const int nt = t1 - t0;
     const int nsteps = G * nt;
-    const bool live = kw < S;                        // the wave has keys
-    const int kwlast = min(kw + 31, S - 1);
+    const bool live = kw < Sk;                       // the wave has keys
+    const int kwlast = min(kw + 31, Sk - 1);
     const int tw0 = live ? ilo_of(kw) / 32 : t1;     // this wave's query tiles [tw0, tw1)
     const int tw1 = live ? ihi_of(kwlast) / 32 + 1 : t1;
     const int ml = (ilo_of(kwlast) + 31) / 32;       // query tiles in [ml, mu) need no mask
     const int mu = (ihi_of(kw) + 1) / 32;
-    const int krow = min(kw + n, S - 1);
+    const int krow = min(kw + n, Sk - 1);
     const int qlo = ilo_of(krow), qhi = ihi_of(krow);  // this lane's key is seen by qlo .. qhi
+    if (nsteps <= 0) {
+        // no query sees a key of this block (keys past the queries' causal
+        // reach, or a window, with fewer queries than keys): dK = dV = 0
+        f32x16 zero[DB];
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) zero[db][r] = 0.f;
+        if (live && kw + n < Sk) {
+            store_t<T, D, DB>(dK + kvhead, kw + n, h, zero, 1.0f);
+            store_t<T, D, DB>(dV + kvhead, kw + n, h, zero, 1.0f);
+        }
+        return;
+    }
 
     // step u: query head kvbh*G + u / nt, query tile t0 + u % nt
     auto stage = [&](auto par, int u) __attribute__((always_inline)) {
         constexpr int P = decltype(par)::value;
-        const int64_t qhead = (int64_t)(kvbh * G + u / nt) * S * D;
+        const int64_t qhead = (int64_t)(kvbh * G + u / nt) * Sq * D;
         const int t = t0 + u % nt;
-        const __amdgpu_buffer_rsrc_t qrs = head_rsrc<T>(Q + qhead, S * RB);
-        const __amdgpu_buffer_rsrc_t ors = head_rsrc<T>(dO + qhead, S * RB);
+        const __amdgpu_buffer_rsrc_t qrs = head_rsrc<T>(Q + qhead, Sq * RB);
+        const __amdgpu_buffer_rsrc_t ors = head_rsrc<T>(dO + qhead, Sq * RB);
         load_tile<T, L, false>(qrb[P], qrs, roff, t * 32, wave, lane);
         load_tile<T, L, true>(qtb[P], qrs, toff, t * 32, wave, lane);
         load_tile<T, L, false>(orb[P], ors, roff, t * 32, wave, lane);
@@ -415,9 +431,9 @@ void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
     const bool ld_lane = wave == 0 && lane < 32;
     auto fetch_ld = [&](auto par, int u) __attribute__((always_inline)) {
         constexpr int P = decltype(par)::value;
-        const int64_t qrow0 = (int64_t)(kvbh * G + u / nt) * S;
-        const __amdgpu_buffer_rsrc_t lrs = __builtin_amdgcn_make_buffer_rsrc((void*)(LSE + qrow0), 0, S * 4, kBufferFlags);
-        const __amdgpu_buffer_rsrc_t drs = __builtin_amdgcn_make_buffer_rsrc((void*)(DELTA + qrow0), 0, S * 4, kBufferFlags);
+        const int64_t qrow0 = (int64_t)(kvbh * G + u / nt) * Sq;
+        const __amdgpu_buffer_rsrc_t lrs = __builtin_amdgcn_make_buffer_rsrc((void*)(LSE + qrow0), 0, Sq * 4, kBufferFlags);
+        const __amdgpu_buffer_rsrc_t drs = __builtin_amdgcn_make_buffer_rsrc((void*)(DELTA + qrow0), 0, Sq * 4, kBufferFlags);
         const int row = (t0 + u % nt) * 32 + n;
         lreg[P] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(lrs, row * 4, 0, 0));
         dreg[P] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(drs, row * 4, 0, 0));
@@ -549,7 +565,7 @@ void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
     }
     wait_vmcnt0();  // the spare stagings of the last steps
 
-    if (live && kw + n < S) {
+    if (live && kw + n < Sk) {
         store_t<T, D, DB>(dK + kvhead, kw + n, h, dkacc, scale);
         store_t<T, D, DB>(dV + kvhead, kw + n, h, dvacc, 1.0f);
     }

@@ -41,7 +41,7 @@ template <int D, bool CAUSAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(F32Cfg<D>::NT, F32Cfg<D>::NT)))
 void fa_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                        const float* __restrict__ V, float* __restrict__ O, float* __restrict__ LSE,
-                       int S, int BH, int n_qblk, int G, int wl, int wr, float c) {
+                       int Sq, int Sk, int BH, int n_qblk, int G, int wl, int wr, float c) {
     constexpr int NW = F32Cfg<D>::NW;
     constexpr int XW = D + 2;  // floats per lane in the merge: acc, m, l
     __shared__ float xch[(NW - 1) * XW * 64];
@@ -55,13 +55,13 @@ void fa_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
     const int qblk = CAUSAL ? (n_qblk - 1 - rank) : rank;
     const int q0 = qblk * F32_BM;
     const int qrow = q0 + lane;
-    const int64_t head = (int64_t)bh * S * D;
-    const int64_t kvhead = (int64_t)(bh / G) * S * D;  // grouped heads: G query heads per K/V head
+    const int64_t head = (int64_t)bh * Sq * D;
+    const int64_t kvhead = (int64_t)(bh / G) * Sk * D;  // grouped heads: G query heads per K/V head
     const float* kh = K + kvhead;
     const float* vh = V + kvhead;
 
     float q[D], acc[D];
-    const int qsrc = min(qrow, S - 1);
+    const int qsrc = min(qrow, Sq - 1);
 #pragma unroll
     for (int d = 0; d < D; ++d) {
         q[d] = Q[head + (int64_t)qsrc * D + d];
@@ -70,16 +70,18 @@ void fa_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
     float m_run = kMInit, l_run = 0.f;
 
     // Keys of row i: lo(i) .. hi(i) -- at most i when causal, i - wl .. i + wr
-    // within a window (wl, wr = -1: no limit on that side).  The block's rows
-    // together see klo .. khi; this wave takes the slice [kb, ke) of it.
-    const int qlast = min(q0 + F32_BM, S) - 1;
+    // within a window (wl, wr = -1: no limit on that side), never past Sk - 1.
+    // The block's rows together see klo .. khi; this wave takes the slice
+    // [kb, ke) of it (empty when the range is: a window can leave rows no key
+    // when there are fewer keys than queries).
+    const int qlast = min(q0 + F32_BM, Sq) - 1;
     const int klo = wl >= 0 ? max(0, q0 - wl) : 0;
-    const int khi = min(CAUSAL ? qlast : S - 1, wr >= 0 ? qlast + wr : S - 1);
+    const int khi = min(min(CAUSAL ? qlast : Sk - 1, wr >= 0 ? qlast + wr : Sk - 1), Sk - 1);
     const int nk = khi - klo + 1;
     const int kb = klo + wave * nk / NW;
     const int ke = klo + (wave + 1) * nk / NW;
     const int lo = wl >= 0 ? max(0, qrow - wl) : 0;
-    const int hi = min(CAUSAL ? qrow : S - 1, wr >= 0 ? qrow + wr : S - 1);
+    const int hi = min(min(CAUSAL ? qrow : Sk - 1, wr >= 0 ? qrow + wr : Sk - 1), Sk - 1);
     for (int key = kb; key < ke; ++key) {
         const float* kr = kh + (int64_t)key * D;
         float part[8];
@@ -131,11 +133,12 @@ void fa_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
         for (int d = 0; d < D; ++d) acc[d] = __builtin_fmaf(aw, x[d * 64], acc[d]);
     }
 
-    if (qrow < S) {
-        const float inv = 1.0f / l;
+    if (qrow < Sq) {
+        // (a row with no key has l = 0 and acc = 0: O = 0, lse = ln2 * log2 0 = -inf)
+        const float inv = l > 0.f ? 1.0f / l : 0.f;
 #pragma unroll
         for (int d = 0; d < D; ++d) O[head + (int64_t)qrow * D + d] = acc[d] * inv;
-        LSE[(int64_t)bh * S + qrow] = kLn2 * (mx + log2_fast(l));
+        LSE[(int64_t)bh * Sq + qrow] = kLn2 * (mx + log2_fast(l));
     }
 }
 

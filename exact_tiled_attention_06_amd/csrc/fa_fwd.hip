@@ -3,9 +3,9 @@
 //
 // Host-side plan ("T5 讲解：FlashAttention forward", sections ② and ⑥;
 // "Triton 实现", section "Grid 与并行策略"): one workgroup per
-// (query block, batch*head), i.e. ceil(S/BM) * B*H independent workgroups with
-// no communication between them; the default scale 1/sqrt(D) is the caller's
-// business (the Python binding supplies it).
+// (query block, batch*head), i.e. ceil(S_q/BM) * B*H independent workgroups
+// with no communication between them; the default scale 1/sqrt(D) is the
+// caller's business (the Python binding supplies it).
 #include <stdint.h>
 #include <string.h>
 
@@ -65,39 +65,56 @@ struct Fwd {
     const void *q, *k, *v;
     void* o;
     float* lse;
-    int S, BH, G;  // G query heads per K/V head
-    int wl, wr;    // window (left, right); -1: no limit on that side
-    float c;       // scale * log2(e)
+    int Sq, Sk, BH, G;  // queries, keys per head; G query heads per K/V head
+    int wl, wr;         // window (left, right); -1: no limit on that side
+    float c;            // scale * log2(e)
     hipStream_t stream;
 };
 
+// Fills n 32-bit words with `value` (outputs of problems without keys or
+// without queries).
+__global__ void fa_fill_kernel(uint32_t* __restrict__ p, uint32_t value, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = value;
+}
+
+int fill_words(void* p, uint32_t value, int64_t bytes, hipStream_t stream) {
+    const int64_t n = bytes / 4;
+    if (n == 0) return FA_OK;
+    const int64_t blocks = (n + 255) / 256;
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(fa_fill_kernel, dim3((unsigned)(blocks < 4096 ? blocks : 4096)), dim3(256), 0, stream,
+                       (uint32_t*)p, value, n);
+    return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
 template <typename T, typename Cfg>
 int launch_cfg(const Fwd& a) {
-    const int n_qblk = (a.S + Cfg::BM - 1) / Cfg::BM;
+    const int n_qblk = (a.Sq + Cfg::BM - 1) / Cfg::BM;
     const int64_t grid = (int64_t)n_qblk * a.BH;
     if (grid > (int64_t)1 << 24) return FA_ERR_TOO_LARGE;
     (void)hipGetLastError();  // clear a stale error so the check below sees this launch only
     if constexpr (Cfg::QB == 2 && Cfg::KB == 1 && Cfg::PIPE)
         hipLaunchKernelGGL((fa_fwd_split_kernel<T, Cfg>), dim3((unsigned)grid), dim3(Cfg::NT), 0, a.stream,
                            (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o,
-                           a.lse, a.S, a.BH, n_qblk, a.G, a.c);
+                           a.lse, a.Sq, a.Sk, a.BH, n_qblk, a.G, a.c);
     else
         hipLaunchKernelGGL((fa_fwd_mfma_kernel<T, Cfg>), dim3((unsigned)grid), dim3(Cfg::NT), 0, a.stream,
                            (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o,
-                           a.lse, a.S, a.BH, n_qblk, a.G, a.c);
+                           a.lse, a.Sq, a.Sk, a.BH, n_qblk, a.G, a.c);
     return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
 // Thin grids: workgroups of NW waves that share BMW query rows and split the keys.
 template <typename T, typename Cfg>
 int launch_ksplit(const Fwd& a) {
-    const int n_qblk = (a.S + Cfg::BMW - 1) / Cfg::BMW;
+    const int n_qblk = (a.Sq + Cfg::BMW - 1) / Cfg::BMW;
     const int64_t grid = (int64_t)n_qblk * a.BH;
     if (grid > (int64_t)1 << 24) return FA_ERR_TOO_LARGE;
     (void)hipGetLastError();
     hipLaunchKernelGGL((fa_fwd_ksplit_kernel<T, Cfg>), dim3((unsigned)grid), dim3(Cfg::NT), 0, a.stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse,
-                       a.S, a.BH, n_qblk, a.G, a.c);
+                       a.Sq, a.Sk, a.BH, n_qblk, a.G, a.c);
     return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
@@ -105,13 +122,13 @@ int launch_ksplit(const Fwd& a) {
 template <typename T, int D, bool CAUSAL>
 int launch_window(const Fwd& a) {
     using Cfg = MfmaConfig<D, CAUSAL, 1, 4, 32, false, 2, 32>;
-    const int n_qblk = (a.S + Cfg::BM - 1) / Cfg::BM;
+    const int n_qblk = (a.Sq + Cfg::BM - 1) / Cfg::BM;
     const int64_t grid = (int64_t)n_qblk * a.BH;
     if (grid > (int64_t)1 << 24) return FA_ERR_TOO_LARGE;
     (void)hipGetLastError();
     hipLaunchKernelGGL((fa_fwd_window_kernel<T, Cfg>), dim3((unsigned)grid), dim3(Cfg::NT), 0, a.stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse,
-                       a.S, a.BH, n_qblk, a.G, a.wl, a.wr, a.c);
+                       a.Sq, a.Sk, a.BH, n_qblk, a.G, a.wl, a.wr, a.c);
     return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
@@ -121,7 +138,7 @@ int launch_mfma(const Fwd& a) {
     using TL = Tiles<D>;
     using Large = MfmaConfig<D, CAUSAL, TL::QB, TL::NW, TL::BN, TL::PIPE, 2, TL::TBN>;
     using Small = MfmaConfig<D, CAUSAL, TL::SMALL_QB, TL::SMALL_NW, TL::SMALL_BN, TL::SMALL_PIPE>;
-    const int64_t large_grid = (int64_t)((a.S + Large::BM - 1) / Large::BM) * a.BH;
+    const int64_t large_grid = (int64_t)((a.Sq + Large::BM - 1) / Large::BM) * a.BH;
     if (large_grid >= kFullGrid) return launch_cfg<T, Large>(a);
     if constexpr (D <= 64) {
         // 64 query rows per workgroup, keys split over 4 waves
@@ -133,13 +150,13 @@ int launch_mfma(const Fwd& a) {
 
 template <int D, bool CAUSAL>
 int launch_f32(const Fwd& a) {
-    const int n_qblk = (a.S + F32_BM - 1) / F32_BM;
+    const int n_qblk = (a.Sq + F32_BM - 1) / F32_BM;
     const int64_t grid = (int64_t)n_qblk * a.BH;
     if (grid > (int64_t)1 << 24) return FA_ERR_TOO_LARGE;
     (void)hipGetLastError();
     hipLaunchKernelGGL((fa_fwd_f32_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(F32Cfg<D>::NT), 0, a.stream,
-                       (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.o, a.lse, a.S, a.BH,
-                       n_qblk, a.G, a.wl, a.wr, a.c);
+                       (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.o, a.lse, a.Sq, a.Sk,
+                       a.BH, n_qblk, a.G, a.wl, a.wr, a.c);
     return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
@@ -170,7 +187,7 @@ struct Bwd {
     const float* lse;
     void *dq, *dk, *dv;
     float* delta;
-    int S, BH, G, wl, wr;
+    int Sq, Sk, BH, G, wl, wr;
     float c, scale;
     hipStream_t stream;
 };
@@ -178,22 +195,21 @@ struct Bwd {
 template <typename T, int D, bool CAUSAL>
 int launch_bwd(const Bwd& a) {
     using Cfg = BwdConfig<D, CAUSAL, 4>;
-    const int n_blk = (a.S + Cfg::BM - 1) / Cfg::BM;     // key blocks (dK/dV kernel)
-    const int n_qblk = (a.S + Cfg::BMQ - 1) / Cfg::BMQ;  // query blocks (dQ kernel)
-    const int64_t grid = (int64_t)n_blk * a.BH;
-    if (grid > (int64_t)1 << 24) return FA_ERR_TOO_LARGE;
+    const int n_blk = (a.Sk + Cfg::BM - 1) / Cfg::BM;     // key blocks (dK/dV kernel)
+    const int n_qblk = (a.Sq + Cfg::BMQ - 1) / Cfg::BMQ;  // query blocks (dQ kernel)
+    if ((int64_t)n_blk * a.BH > (int64_t)1 << 24 || (int64_t)n_qblk * a.BH > (int64_t)1 << 24) return FA_ERR_TOO_LARGE;
     const int BHkv = a.BH / a.G;
     (void)hipGetLastError();
     // dQ (and D = rowsum(dO o O) into `delta`), then dK and dV, which read D
     hipLaunchKernelGGL((fa_bwd_dq_kernel<T, Cfg>), dim3((unsigned)((int64_t)n_qblk * a.BH)), dim3(Cfg::NT), 0,
                        a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                       (const uint16_t*)a.o, (const uint16_t*)a.dout, a.lse, (uint16_t*)a.dq, a.delta, a.S, a.BH,
-                       n_qblk, a.G, a.wl, a.wr, a.c, a.scale);
+                       (const uint16_t*)a.o, (const uint16_t*)a.dout, a.lse, (uint16_t*)a.dq, a.delta, a.Sq, a.Sk,
+                       a.BH, n_qblk, a.G, a.wl, a.wr, a.c, a.scale);
     if (hipGetLastError() != hipSuccess) return FA_ERR_LAUNCH;
     hipLaunchKernelGGL((fa_bwd_dkdv_kernel<T, Cfg>), dim3((unsigned)((int64_t)n_blk * BHkv)), dim3(Cfg::NT), 0,
                        a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                       (const uint16_t*)a.dout, a.lse, (const float*)a.delta, (uint16_t*)a.dk, (uint16_t*)a.dv, a.S,
-                       BHkv, n_blk, a.G, a.wl, a.wr, a.c, a.scale);
+                       (const uint16_t*)a.dout, a.lse, (const float*)a.delta, (uint16_t*)a.dk, (uint16_t*)a.dv, a.Sq,
+                       a.Sk, BHkv, n_blk, a.G, a.wl, a.wr, a.c, a.scale);
     return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
@@ -213,9 +229,10 @@ int dispatch_bwd(int64_t D, int dtype, const Bwd& a) {
 
 // Checks shared by the entry points (no HIP call): shapes, head dim, grouped
 // heads (H a multiple of H_kv), causal flag, window bounds, scale.
-int check_problem(int64_t B, int64_t H, int64_t H_kv, int64_t S, int64_t D, int causal, int64_t wl, int64_t wr,
-                  float scale) {
-    if (B < 0 || H < 0 || S < 0 || H_kv < 0 || (H_kv == 0 ? H != 0 : H % H_kv != 0)) return FA_ERR_SHAPE;
+int check_problem(int64_t B, int64_t H, int64_t H_kv, int64_t Sq, int64_t Sk, int64_t D, int causal, int64_t wl,
+                  int64_t wr, float scale) {
+    if (B < 0 || H < 0 || Sq < 0 || Sk < 0 || H_kv < 0 || (H_kv == 0 ? H != 0 : H % H_kv != 0))
+        return FA_ERR_SHAPE;
     if (D != 16 && D != 32 && D != 64 && D != 128) return FA_ERR_HEAD_DIM;
     if (causal != 0 && causal != 1) return FA_ERR_CAUSAL;
     if (wl < -1 || wr < -1) return FA_ERR_WINDOW;
@@ -227,7 +244,8 @@ int check_problem(int64_t B, int64_t H, int64_t H_kv, int64_t S, int64_t D, int 
     return FA_OK;
 }
 
-// Index ranges shared by the entry points; H_kv > 0 here.
+// Index ranges shared by the entry points (S: the longer of the query and key
+// lengths, > 0); H_kv > 0 here.
 int check_sizes(int64_t B, int64_t H, int64_t S, int64_t D) {
     const int64_t kMaxInt = 2147483647;
     if (B > kMaxInt || H > kMaxInt || B * H > kMaxInt / 2 || S > (kMaxInt >> 1)) return FA_ERR_TOO_LARGE;
@@ -236,27 +254,29 @@ int check_sizes(int64_t B, int64_t H, int64_t S, int64_t D) {
     return FA_OK;
 }
 
-// The window's limits clipped to the sequence: a side that reaches past S is
-// the same as no limit.
+// The window's limits clipped to the sequences: a side that reaches past both
+// the queries and the keys (S = max(S_q, S_k)) is the same as no limit.
 int clip_window(int64_t w, int64_t S) { return (w < 0 || w >= S) ? -1 : (int)w; }
 
 }  // namespace
 
 extern "C" int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const void* dout,
                          const float* lse, void* dq, void* dk, void* dv, float* delta, int64_t B, int64_t H,
-                         int64_t H_kv, int64_t S, int64_t D, int causal, int64_t window_left,
+                         int64_t H_kv, int64_t S_q, int64_t S_k, int64_t D, int causal, int64_t window_left,
                          int64_t window_right, float scale, int dtype, void* stream) {
     // ---- argument checks: no HIP call before all of them pass ----------------
-    int rc = check_problem(B, H, H_kv, S, D, causal, window_left, window_right, scale);
+    int rc = check_problem(B, H, H_kv, S_q, S_k, D, causal, window_left, window_right, scale);
     if (rc == FA_ERR_SHAPE || rc == FA_ERR_HEAD_DIM) return rc;
     if (dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
     if (rc != FA_OK) return rc;
-    if (B == 0 || H == 0 || S == 0) return FA_OK;
-    if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !delta) return FA_ERR_NULL_POINTER;
+    if (B == 0 || H == 0 || (S_q == 0 && S_k == 0)) return FA_OK;
+    if (S_q > 0 && (!q || !o || !dout || !lse || !dq || !delta)) return FA_ERR_NULL_POINTER;
+    if (S_k > 0 && (!k || !v || !dk || !dv)) return FA_ERR_NULL_POINTER;
+    const int64_t S = S_q > S_k ? S_q : S_k;
     if ((rc = check_sizes(B, H, S, D)) != FA_OK) return rc;
     if (S * D * 2 > 2147483647) return FA_ERR_TOO_LARGE;
     const int64_t BH = B * H;
-    const int64_t tb = BH * S * D * 2, kvb = B * H_kv * S * D * 2, vb = BH * S * 4;
+    const int64_t tb = BH * S_q * D * 2, kvb = B * H_kv * S_k * D * 2, vb = BH * S_q * 4;
     if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)dout | (uintptr_t)dq |
          (uintptr_t)dk | (uintptr_t)dv) & 15)
         return FA_ERR_ALIGNMENT;
@@ -270,7 +290,13 @@ extern "C" int fa_bwd_ex(const void* q, const void* k, const void* v, const void
         for (int j = 0; j < 10; ++j)
             if (j != 6 + i && overlaps(outs[i], out_bytes[i], all[j], all_bytes[j])) return FA_ERR_ALIAS;
 
-    Bwd a{q, k, v, o, dout, lse, dq, dk, dv, delta, (int)S, (int)BH, (int)(H / H_kv),
+    // no keys: every dQ is 0 (dK, dV are empty); no queries: dK = dV = 0
+    if (S_k == 0) return fill_words(dq, 0u, tb, (hipStream_t)stream);
+    if (S_q == 0) {
+        if ((rc = fill_words(dk, 0u, kvb, (hipStream_t)stream)) != FA_OK) return rc;
+        return fill_words(dv, 0u, kvb, (hipStream_t)stream);
+    }
+    Bwd a{q, k, v, o, dout, lse, dq, dk, dv, delta, (int)S_q, (int)S_k, (int)BH, (int)(H / H_kv),
           clip_window(window_left, S), clip_window(window_right, S),
           (float)((double)scale * 1.4426950408889634), scale, (hipStream_t)stream};
     return causal ? dispatch_bwd<true>(D, dtype, a) : dispatch_bwd<false>(D, dtype, a);
@@ -279,27 +305,29 @@ extern "C" int fa_bwd_ex(const void* q, const void* k, const void* v, const void
 extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                       const float* lse, void* dq, void* dk, void* dv, float* delta, int64_t B, int64_t H,
                       int64_t S, int64_t D, int causal, float scale, int dtype, void* stream) {
-    return fa_bwd_ex(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, H, S, D, causal, -1, -1, scale, dtype, stream);
+    return fa_bwd_ex(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, H, S, S, D, causal, -1, -1, scale, dtype,
+                     stream);
 }
 
 extern "C" int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
-                         int64_t H_kv, int64_t S, int64_t D, int causal, int64_t window_left, int64_t window_right,
-                         float scale, int dtype, void* stream) {
+                         int64_t H_kv, int64_t S_q, int64_t S_k, int64_t D, int causal, int64_t window_left,
+                         int64_t window_right, float scale, int dtype, void* stream) {
     // ---- argument checks: no HIP call before all of them pass ----------------
-    int rc = check_problem(B, H, H_kv, S, D, causal, window_left, window_right, scale);
+    int rc = check_problem(B, H, H_kv, S_q, S_k, D, causal, window_left, window_right, scale);
     if (rc == FA_ERR_SHAPE || rc == FA_ERR_HEAD_DIM) return rc;
     if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
     if (rc != FA_OK) return rc;
-    if (B == 0 || H == 0 || S == 0) return FA_OK;  // empty problem: nothing to compute
-    if (!q || !k || !v || !o || !lse) return FA_ERR_NULL_POINTER;
+    if (B == 0 || H == 0 || S_q == 0) return FA_OK;  // no query row: nothing to write
+    if (!q || !o || !lse || (S_k > 0 && (!k || !v))) return FA_ERR_NULL_POINTER;
+    const int64_t S = S_q > S_k ? S_q : S_k;
     if ((rc = check_sizes(B, H, S, D)) != FA_OK) return rc;
     // the matrix-core kernels address one head's K or V rows through a buffer
-    // resource with a 32-bit extent: S * D * 2 bytes must stay below 2^31
+    // resource with a 32-bit extent: S_k * D * 2 bytes must stay below 2^31
     if (dtype != FA_DTYPE_F32 && S * D * 2 > 2147483647) return FA_ERR_TOO_LARGE;
     const int64_t BH = B * H;
-    const int64_t tensor_bytes = BH * S * D * elem_size(dtype);
-    const int64_t kv_bytes = B * H_kv * S * D * elem_size(dtype);
-    const int64_t lse_bytes = BH * S * 4;
+    const int64_t tensor_bytes = BH * S_q * D * elem_size(dtype);
+    const int64_t kv_bytes = B * H_kv * S_k * D * elem_size(dtype);
+    const int64_t lse_bytes = BH * S_q * 4;
     if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15) return FA_ERR_ALIGNMENT;
     if (((uintptr_t)lse) & 3) return FA_ERR_ALIGNMENT;
     if (overlaps(o, tensor_bytes, q, tensor_bytes) || overlaps(o, tensor_bytes, k, kv_bytes) ||
@@ -308,22 +336,27 @@ extern "C" int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, f
         overlaps(lse, lse_bytes, v, kv_bytes))
         return FA_ERR_ALIAS;
 
+    // no keys: every row is empty, O = 0 and lse = ln 0 = -inf
+    if (S_k == 0) {
+        if ((rc = fill_words(o, 0u, tensor_bytes, (hipStream_t)stream)) != FA_OK) return rc;
+        return fill_words(lse, 0xFF800000u, lse_bytes, (hipStream_t)stream);
+    }
     // c = scale * log2(e), rounded once to fp32: scores enter exp2 as S*c - m.
-    Fwd a{q, k, v, o, lse, (int)S, (int)BH, (int)(H / H_kv), clip_window(window_left, S),
+    Fwd a{q, k, v, o, lse, (int)S_q, (int)S_k, (int)BH, (int)(H / H_kv), clip_window(window_left, S),
           clip_window(window_right, S), (float)((double)scale * 1.4426950408889634), (hipStream_t)stream};
     return causal ? dispatch_d<true>(D, dtype, a) : dispatch_d<false>(D, dtype, a);
 }
 
 extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
                       int64_t S, int64_t D, int causal, float scale, int dtype, void* stream) {
-    return fa_fwd_ex(q, k, v, o, lse, B, H, H, S, D, causal, -1, -1, scale, dtype, stream);
+    return fa_fwd_ex(q, k, v, o, lse, B, H, H, S, S, D, causal, -1, -1, scale, dtype, stream);
 }
 
 extern "C" const char* fa_status_string(int status) {
     switch (status) {
         case FA_OK: return "ok";
         case FA_ERR_NULL_POINTER: return "a tensor pointer is NULL";
-        case FA_ERR_SHAPE: return "B, H, S must be >= 0 and H a multiple of H_kv";
+        case FA_ERR_SHAPE: return "B, H, S_q, S_k must be >= 0 and H a multiple of H_kv";
         case FA_ERR_HEAD_DIM: return "head dim D must be 16, 32, 64 or 128";
         case FA_ERR_DTYPE: return "dtype must be FA_DTYPE_F32, FA_DTYPE_F16 or FA_DTYPE_BF16";
         case FA_ERR_CAUSAL: return "causal must be 0 or 1";

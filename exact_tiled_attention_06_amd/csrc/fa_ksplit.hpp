@@ -48,7 +48,7 @@ template <typename T, typename Cfg>
 __global__ __attribute__((amdgpu_flat_work_group_size(Cfg::NT, Cfg::NT), amdgpu_waves_per_eu(Cfg::OCC, Cfg::OCC)))
 void fa_fwd_ksplit_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                           const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
-                          int S, int BH, int n_qblk, int G, float c) {
+                          int Sq, int Sk, int BH, int n_qblk, int G, float c) {
     using W = WaveTile<T, Cfg>;
     using L = WaveLoader<Cfg>;
     constexpr int D = Cfg::D, QB = Cfg::QB, KB = Cfg::KB, KS = Cfg::KS, DB = Cfg::DB;
@@ -79,17 +79,17 @@ void fa_fwd_ksplit_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     const int qblk = CAUSAL ? (n_qblk - 1 - rank) : rank;
     const int q0 = qblk * BMW;
 
-    const int64_t head = (int64_t)bh * S * D;
-    const int64_t kvhead = (int64_t)(bh / G) * S * D;  // grouped heads: G query heads per K/V head
+    const int64_t head = (int64_t)bh * Sq * D;
+    const int64_t kvhead = (int64_t)(bh / G) * Sk * D;  // grouped heads: G query heads per K/V head
     const uint16_t* qh = Q + head;
-    const __amdgpu_buffer_rsrc_t krs = head_rsrc<T>(K + kvhead, S * RB);
-    const __amdgpu_buffer_rsrc_t vrs = head_rsrc<T>(V + kvhead, S * RB);
+    const __amdgpu_buffer_rsrc_t krs = head_rsrc<T>(K + kvhead, Sk * RB);
+    const __amdgpu_buffer_rsrc_t vrs = head_rsrc<T>(V + kvhead, Sk * RB);
     uint32_t koff[L::PER], voff[L::PER];
     L::template offsets<false>(lane, koff);
     L::template offsets<true>(lane, voff);
 
     // This wave's slice [tb, te) of the block's key tiles.
-    const int kend = CAUSAL ? min(q0 + BMW, S) : S;
+    const int kend = CAUSAL ? min(q0 + BMW, Sk) : Sk;
     const int ntiles = (kend + BN - 1) / BN;
     const int tb = wave * ntiles / NW;
     const int te = (wave + 1) * ntiles / NW;
@@ -99,8 +99,8 @@ void fa_fwd_ksplit_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     int last[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-        const int qrow = min(q0 + qb * 32 + n, S - 1);
-        last[qb] = CAUSAL ? qrow : S - 1;
+        const int qrow = min(q0 + qb * 32 + n, Sq - 1);
+        last[qb] = CAUSAL ? min(qrow, Sk - 1) : Sk - 1;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             qf[qb][ks] = *reinterpret_cast<const u32x4*>(qh + (int64_t)qrow * D + ks * 16 + h * 8);
@@ -147,7 +147,7 @@ void fa_fwd_ksplit_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
 
         // rows whose tiles need no mask: tiles before the block's first row
         // and before the end of the sequence
-        const int unmasked = min(CAUSAL ? (q0 + 1) / BN : ntiles, S / BN);
+        const int unmasked = min(CAUSAL ? (q0 + 1) / BN : ntiles, Sk / BN);
         auto iter = [&](auto kind, int u, FA_LDS char* kc, FA_LDS char* kn, FA_LDS char* vc, FA_LDS char* vp,
                         f32x16 (&s_cur)[QB][KB], f32x16 (&s_nxt)[QB][KB], u32x4 (&p_prv)[QB][KB][2],
                         u32x4 (&p_cur)[QB][KB][2]) __attribute__((always_inline)) {
@@ -159,7 +159,7 @@ void fa_fwd_ksplit_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
             L::template load<T>(vc, vrs, voff, k0);
             if constexpr (KIND == 0) {
                 if (u + 1 < nt) W::qk(kn, offk, qf, s_nxt);
-                if ((CAUSAL && k0 + BN - 1 > q0) || k0 + BN > S) W::mask(s_cur, last, k0, h);
+                if ((CAUSAL && k0 + BN - 1 > q0) || k0 + BN > Sk) W::mask(s_cur, last, k0, h);
                 W::first(s_cur, m_run, l_run, c, p_cur);
                 return;
             }
@@ -169,7 +169,7 @@ void fa_fwd_ksplit_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
             } else {
                 if (u + 1 < nt) W::qk(kn, offk, qf, s_nxt);
                 W::pv(vp, offv, p_prv, oacc);
-                if ((CAUSAL && k0 + BN - 1 > q0) || k0 + BN > S) W::mask(s_cur, last, k0, h);
+                if ((CAUSAL && k0 + BN - 1 > q0) || k0 + BN > Sk) W::mask(s_cur, last, k0, h);
                 W::expo(s_cur, m_run, c, p_cur, rs);
             }
             if (W::needs_rescale(rs)) W::rescale(s_cur, m_run, l_run, oacc, c, p_cur, rs);
@@ -246,13 +246,13 @@ void fa_fwd_ksplit_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     }
 
     uint16_t* oh = O + head;
-    float* lh = LSE + (int64_t)bh * S;
+    float* lh = LSE + (int64_t)bh * Sq;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         const float l = halves_sum(l_run[qb]);
         const float inv = 1.0f / l;
         const int qrow = q0 + qb * 32 + n;
-        if (qrow < S) {
+        if (qrow < Sq) {
 #pragma unroll
             for (int db = 0; db < DB; ++db)
 #pragma unroll

@@ -424,7 +424,7 @@ template <typename T, typename Cfg>
 __global__ __attribute__((amdgpu_flat_work_group_size(Cfg::NT, Cfg::NT), amdgpu_waves_per_eu(Cfg::OCC, Cfg::OCC)))
 void fa_fwd_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                         const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
-                        int S, int BH, int n_qblk, int G, float c) {
+                        int Sq, int Sk, int BH, int n_qblk, int G, float c) {
     using W = WaveTile<T, Cfg>;
     constexpr int D = Cfg::D, QB = Cfg::QB, KB = Cfg::KB, KS = Cfg::KS, DB = Cfg::DB;
     constexpr int BN = Cfg::BN, BM = Cfg::BM, BMW = Cfg::BMW, RB = Cfg::RB;
@@ -454,19 +454,19 @@ void fa_fwd_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
     const int q0 = qblk * BM;
     const int qw = q0 + wave * BMW;
 
-    const int64_t head = (int64_t)bh * S * D;
-    const int64_t kvhead = (int64_t)(bh / G) * S * D;  // grouped heads: G query heads per K/V head
+    const int64_t head = (int64_t)bh * Sq * D;
+    const int64_t kvhead = (int64_t)(bh / G) * Sk * D;  // grouped heads: G query heads per K/V head
     const uint16_t* qh = Q + head;
-    const __amdgpu_buffer_rsrc_t krs = head_rsrc<T>(K + kvhead, S * RB);
-    const __amdgpu_buffer_rsrc_t vrs = head_rsrc<T>(V + kvhead, S * RB);
+    const __amdgpu_buffer_rsrc_t krs = head_rsrc<T>(K + kvhead, Sk * RB);
+    const __amdgpu_buffer_rsrc_t vrs = head_rsrc<T>(V + kvhead, Sk * RB);
     const uint32_t koff = tile_lane_offset<Cfg, false>(wave, lane);
     const uint32_t voff = tile_lane_offset<Cfg, true>(wave, lane);
 
-    const int kend = CAUSAL ? min(q0 + BM, S) : S;
+    const int kend = CAUSAL ? min(q0 + BM, Sk) : Sk;
     const int ntiles = (kend + BN - 1) / BN;
     // tiles this wave attends to (its last query's diagonal for causal)
-    const int wend = CAUSAL ? min(qw + BMW, S) : S;
-    const int wtiles = qw < S ? min(ntiles, (wend + BN - 1) / BN) : 0;
+    const int wend = CAUSAL ? min(qw + BMW, Sk) : Sk;
+    const int wtiles = qw < Sq ? min(ntiles, (wend + BN - 1) / BN) : 0;
 
     // First tiles in flight before anything else: K(0) and, pipelined, K(1);
     // otherwise K(0) and V(0).
@@ -483,8 +483,8 @@ void fa_fwd_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
     int last[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-        const int qrow = min(qw + qb * 32 + n, S - 1);
-        last[qb] = CAUSAL ? qrow : S - 1;
+        const int qrow = min(qw + qb * 32 + n, Sq - 1);
+        last[qb] = CAUSAL ? min(qrow, Sk - 1) : Sk - 1;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
             qf[qb][ks] = *reinterpret_cast<const u32x4*>(qh + (int64_t)qrow * D + ks * 16 + h * 8);
@@ -547,7 +547,7 @@ void fa_fwd_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
                 if (t >= wtiles) break;  // wave-uniform
                 const int k0 = t * BN;
                 W::qk(kc + sub * BN * RB, offk, qf, sA);
-                if ((CAUSAL && k0 + BN - 1 > qw) || k0 + BN > S) W::mask(sA, last, k0, h);
+                if ((CAUSAL && k0 + BN - 1 > qw) || k0 + BN > Sk) W::mask(sA, last, k0, h);
                 if (t == 0) {
                     W::first(sA, m_run, l_run, c, pA);
                 } else {
@@ -586,7 +586,7 @@ void fa_fwd_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
             if constexpr (KIND == 0) {
                 if (t >= wtiles) return;
                 if (t + 1 < wtiles) W::qk(kn, offk, qf, s_nxt);
-                if ((CAUSAL && k0 + BN - 1 > qw) || k0 + BN > S) W::mask(s_cur, last, k0, h);
+                if ((CAUSAL && k0 + BN - 1 > qw) || k0 + BN > Sk) W::mask(s_cur, last, k0, h);
                 W::first(s_cur, m_run, l_run, c, p_cur);
                 return;
             }
@@ -602,7 +602,7 @@ void fa_fwd_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
                 }
                 if (do_qk) W::qk(kn, offk, qf, s_nxt);
                 W::pv(vp, offv, p_prv, oacc);
-                if ((CAUSAL && k0 + BN - 1 > qw) || k0 + BN > S) W::mask(s_cur, last, k0, h);
+                if ((CAUSAL && k0 + BN - 1 > qw) || k0 + BN > Sk) W::mask(s_cur, last, k0, h);
                 W::expo(s_cur, m_run, c, p_cur, rs);
             }
             // P*V of tile t-1 is in acc now, so a rescale covers every earlier term.
@@ -615,7 +615,7 @@ void fa_fwd_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
         using Edge = std::integral_constant<int, 2>;
 
         // leading tiles that need no mask for any of this wave's rows
-        const int unmasked = min(CAUSAL ? (qw + 1) / BN : ntiles, S / BN);
+        const int unmasked = min(CAUSAL ? (qw + 1) / BN : ntiles, Sk / BN);
         const int steady_end = min(wtiles - 1, unmasked);  // steady for 1 <= t < steady_end
 
         iter(First{}, 0, kbuf[0], kbuf[1], vbuf[0], vbuf[1], sA, sB, pA, pB);
@@ -639,13 +639,13 @@ void fa_fwd_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
 
     // ---- epilogue: O = acc / l, lse = ln2 * (m + log2 l) ---------------------------
     uint16_t* oh = O + head;
-    float* lh = LSE + (int64_t)bh * S;
+    float* lh = LSE + (int64_t)bh * Sq;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         const float l = halves_sum(l_run[qb]);
         const float inv = 1.0f / l;
         const int qrow = qw + qb * 32 + n;
-        if (qrow < S) {
+        if (qrow < Sq) {
 #pragma unroll
             for (int db = 0; db < DB; ++db)
 #pragma unroll

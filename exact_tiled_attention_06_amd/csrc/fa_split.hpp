@@ -154,7 +154,7 @@ struct SplitTile {
 template <typename T, typename Cfg>
 __global__ __attribute__((amdgpu_flat_work_group_size(Cfg::NT, Cfg::NT), amdgpu_waves_per_eu(Cfg::OCC, Cfg::OCC)))
 void fa_fwd_split_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-                         const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE, int S,
+                         const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE, int Sq, int Sk,
                          int BH, int n_qblk, int G, float c) {
     using ST = SplitTile<T, Cfg>;
     constexpr int D = Cfg::D, KS = Cfg::KS, DB = Cfg::DB;
@@ -192,15 +192,15 @@ void fa_fwd_split_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
     const int q0 = qblk * BM;
     const int qw = q0 + wave * BMW;
 
-    const int64_t head = (int64_t)bh * S * D;
-    const int64_t kvhead = (int64_t)(bh / G) * S * D;  // grouped heads: G query heads per K/V head
+    const int64_t head = (int64_t)bh * Sq * D;
+    const int64_t kvhead = (int64_t)(bh / G) * Sk * D;  // grouped heads: G query heads per K/V head
     const uint16_t* qh = Q + head;
-    const __amdgpu_buffer_rsrc_t krs = head_rsrc<T>(K + kvhead, S * RB);
-    const __amdgpu_buffer_rsrc_t vrs = head_rsrc<T>(V + kvhead, S * RB);
+    const __amdgpu_buffer_rsrc_t krs = head_rsrc<T>(K + kvhead, Sk * RB);
+    const __amdgpu_buffer_rsrc_t vrs = head_rsrc<T>(V + kvhead, Sk * RB);
     const uint32_t koff = tile_lane_offset<Cfg, false>(wave, lane);
     const uint32_t voff = tile_lane_offset<Cfg, true>(wave, lane);
 
-    const int ntiles = ((CAUSAL ? min(q0 + BM, S) : S) + BN - 1) / BN;
+    const int ntiles = ((CAUSAL ? min(q0 + BM, Sk) : Sk) + BN - 1) / BN;
     const int nlds = (ntiles + SUB - 1) / SUB;
 
     // Per column block a (rows qw + 32a ..): wt = tiles it attends to, um =
@@ -209,10 +209,10 @@ void fa_fwd_split_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
 #pragma unroll
     for (int a = 0; a < 2; ++a) {
         const int r0 = qw + 32 * a;
-        const int rend = CAUSAL ? min(r0 + 32, S) : S;
-        wt[a] = r0 < S ? min(ntiles, (rend + BN - 1) / BN) : 0;
-        um[a] = min(CAUSAL ? (r0 + 1) / BN : ntiles, S / BN);
-        last[a] = CAUSAL ? min(r0 + n, S - 1) : S - 1;
+        const int rend = CAUSAL ? min(r0 + 32, Sk) : Sk;
+        wt[a] = r0 < Sq ? min(ntiles, (rend + BN - 1) / BN) : 0;
+        um[a] = min(CAUSAL ? (r0 + 1) / BN : ntiles, Sk / BN);
+        last[a] = CAUSAL ? min(r0 + n, Sk - 1) : Sk - 1;
     }
 
     // Prologue transfers: K(0) (this wave's share of its BN rows), K tile 0, V tile 0.
@@ -229,7 +229,7 @@ void fa_fwd_split_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
     u32x4 qf[2][KS];
 #pragma unroll
     for (int a = 0; a < 2; ++a) {
-        const int qrow = min(qw + 32 * a + n, S - 1);
+        const int qrow = min(qw + 32 * a + n, Sq - 1);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             qf[a][ks] = *reinterpret_cast<const u32x4*>(qh + (int64_t)qrow * D + ks * 16 + h * 8);
@@ -372,13 +372,13 @@ void fa_fwd_split_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
 
     // ---- epilogue: O = acc / l, lse = ln2 * (m + log2 l) ---------------------------
     uint16_t* oh = O + head;
-    float* lh = LSE + (int64_t)bh * S;
+    float* lh = LSE + (int64_t)bh * Sq;
 #pragma unroll
     for (int a = 0; a < 2; ++a) {
         const float l = halves_sum(l_run[a]);
         const float inv = 1.0f / l;
         const int qrow = qw + 32 * a + n;
-        if (qrow < S) {
+        if (qrow < Sq) {
 #pragma unroll
             for (int db = 0; db < DB; ++db)
 #pragma unroll

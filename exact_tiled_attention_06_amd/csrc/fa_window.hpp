@@ -24,7 +24,7 @@ template <typename T, typename Cfg>
 __global__ __attribute__((amdgpu_flat_work_group_size(Cfg::NT, Cfg::NT), amdgpu_waves_per_eu(2, 2)))
 void fa_fwd_window_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                           const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
-                          int S, int BH, int n_qblk, int G, int wl, int wr, float c) {
+                          int Sq, int Sk, int BH, int n_qblk, int G, int wl, int wr, float c) {
     using W = WaveTile<T, Cfg>;
     constexpr int D = Cfg::D, KS = Cfg::KS, DB = Cfg::DB, RB = Cfg::RB, BM = Cfg::BM, BN = Cfg::BN;
     constexpr bool CAUSAL = Cfg::CAUSAL;
@@ -49,27 +49,28 @@ void fa_fwd_window_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     const int q0 = qblk * BM;
     const int qw = q0 + 32 * wave;
 
-    const int64_t head = (int64_t)bh * S * D;
-    const int64_t kvhead = (int64_t)(bh / G) * S * D;
-    const __amdgpu_buffer_rsrc_t krs = head_rsrc<T>(K + kvhead, S * RB);
-    const __amdgpu_buffer_rsrc_t vrs = head_rsrc<T>(V + kvhead, S * RB);
+    const int64_t head = (int64_t)bh * Sq * D;
+    const int64_t kvhead = (int64_t)(bh / G) * Sk * D;
+    const __amdgpu_buffer_rsrc_t krs = head_rsrc<T>(K + kvhead, Sk * RB);
+    const __amdgpu_buffer_rsrc_t vrs = head_rsrc<T>(V + kvhead, Sk * RB);
     const uint32_t koff = tile_lane_offset<Cfg, false>(wave, lane);
     const uint32_t voff = tile_lane_offset<Cfg, true>(wave, lane);
 
-    // keys of row i: lo(i) .. hi(i)
+    // keys of row i: lo(i) .. hi(i), an empty range when a window leaves the
+    // row no key (only possible with fewer keys than queries)
     auto lo_of = [&](int i) { return wl >= 0 ? max(0, i - wl) : 0; };
-    auto hi_of = [&](int i) { return min(CAUSAL ? i : S - 1, wr >= 0 ? i + wr : S - 1); };
-    const int qlast = min(q0 + BM, S) - 1;
+    auto hi_of = [&](int i) { return min(min(CAUSAL ? i : Sk - 1, wr >= 0 ? i + wr : Sk - 1), Sk - 1); };
+    const int qlast = min(q0 + BM, Sq) - 1;
     const int tb = lo_of(q0) / BN;              // the workgroup's key tiles [tb, te)
     const int te = hi_of(qlast) / BN + 1;
-    const bool live = qw < S;
-    const int wlast = min(qw + 31, S - 1);
+    const bool live = qw < Sq;
+    const int wlast = min(qw + 31, Sq - 1);
     const int wb = live ? lo_of(qw) / BN : te;   // this wave's tiles [wb, we)
     const int we = live ? hi_of(wlast) / BN + 1 : te;
     // tiles in [ml, mu) lie inside every row's window: no mask
     const int ml = (lo_of(wlast) + BN - 1) / BN;
     const int mu = (hi_of(qw) + 1) / BN;
-    const int qrow = min(qw + n, S - 1);
+    const int qrow = min(qw + n, Sq - 1);
     const int first = lo_of(qrow), last = hi_of(qrow);
 
     load_tile<T, Cfg, false>(kbuf[0], krs, koff, tb * BN, wave, lane);
@@ -141,9 +142,10 @@ void fa_fwd_window_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     if (t < te) step(P0{}, t);
 
     // ---- epilogue: O = acc / l, lse = ln2 * (m + log2 l) ---------------------------
+    // (a row with no key has l = 0 and acc = 0: O = 0 and lse = ln2 * log2 0 = -inf)
     const float l = halves_sum(l_run[0]);
-    const float inv = 1.0f / l;
-    if (qw + n < S) {
+    const float inv = l > 0.f ? 1.0f / l : 0.f;
+    if (qw + n < Sq) {
         uint16_t* oh = O + head;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
@@ -157,7 +159,7 @@ void fa_fwd_window_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
                     *reinterpret_cast<u32x2*>(oh + (int64_t)(qw + n) * D + d) = w;
                 }
             }
-        if (h == 0) LSE[(int64_t)bh * S + qw + n] = kLn2 * (m_run[0] + log2_fast(l));
+        if (h == 0) LSE[(int64_t)bh * Sq + qw + n] = kLn2 * (m_run[0] + log2_fast(l));
     }
 }
 

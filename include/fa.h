@@ -42,7 +42,7 @@ extern "C" {
 /* ---- status codes ------------------------------------------------------- */
 #define FA_OK 0
 #define FA_ERR_NULL_POINTER 1   /* a tensor pointer is NULL for a non-empty problem */
-#define FA_ERR_SHAPE 2          /* B, H or S is negative, or H is not a multiple of H_kv */
+#define FA_ERR_SHAPE 2          /* B, H, S (S_q, S_k) negative, or H not a multiple of H_kv */
 #define FA_ERR_HEAD_DIM 3       /* D is not 16, 32, 64 or 128 */
 #define FA_ERR_DTYPE 4          /* dtype is not FA_DTYPE_F32 / _F16 / _BF16 (fa_bwd: _F16 / _BF16) */
 #define FA_ERR_CAUSAL 5         /* causal is not 0 or 1 */
@@ -139,34 +139,47 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *o, const voi
            int causal, float scale, int dtype, void *stream);
 
 /*
- * fa_fwd_ex, fa_bwd_ex -- fa_fwd and fa_bwd with grouped key/value heads and a
- * sliding window ("Inside FlashAttention", section 6.1: MQA / GQA pass K and V
- * with fewer heads instead of replicating them; window_size = (left, right)
- * limits each query to nearby keys, and whole blocks outside the window are
- * skipped like the blocks above the causal diagonal).
+ * fa_fwd_ex, fa_bwd_ex -- fa_fwd and fa_bwd with grouped key/value heads, a
+ * sliding window, and queries and keys of different length ("Inside
+ * FlashAttention", section 6.1: MQA / GQA pass K and V with fewer heads instead
+ * of replicating them; window_size = (left, right) limits each query to nearby
+ * keys, and whole blocks outside the window are skipped like the blocks above
+ * the causal diagonal; the CS336 write-up's forward kernel for separate query
+ * and key counts, with keys past the key count absent and the causal test on
+ * absolute positions).
  *
- *   H_kv          key/value heads: k, v (and dk, dv) are [B,H_kv,S,D]; H must
- *                 be a multiple of H_kv, and query head h reads key/value head
- *                 h / (H / H_kv).  H_kv = H is plain multi-head attention,
+ *   H_kv          key/value heads: k, v (and dk, dv) are [B,H_kv,S_k,D]; H
+ *                 must be a multiple of H_kv, and query head h reads key/value
+ *                 head h / (H / H_kv).  H_kv = H is plain multi-head attention,
  *                 H_kv = 1 is MQA.  The backward sums each shared head's dK and
  *                 dV over its H / H_kv query heads.
+ *   S_q, S_k      query rows and key rows per head: q, o, dout, dq are
+ *                 [B,H,S_q,D], lse and delta [B,H,S_q], k, v, dk, dv
+ *                 [B,H_kv,S_k,D].  Query i and key j sit at positions i and j.
  *   window_left,  query i attends to keys i - window_left .. i + window_right
  *   window_right  (and, when causal, to none past i); -1 leaves that side
- *                 unlimited.  A bound of S or more is the same as -1.
+ *                 unlimited.  A bound of max(S_q, S_k) or more is the same as -1.
  *   every other argument as for fa_fwd / fa_bwd; fa_fwd(...) is
- *   fa_fwd_ex(..., H_kv = H, ..., window_left = window_right = -1, ...), and
- *   likewise fa_bwd.
+ *   fa_fwd_ex(..., H_kv = H, S_q = S_k = S, ..., window_left = window_right =
+ *   -1, ...), and likewise fa_bwd.
+ *
+ * A query row that attends to no key (S_k = 0, or a window that leaves the row
+ * none, possible only when S_k < S_q) gets O = 0 and lse = -inf (the log of an
+ * empty sum); its dQ is 0 and it adds nothing to dK, dV.  With S_q = 0 the
+ * backward writes dK = dV = 0; with S_k = 0 it writes dQ = 0 and leaves delta
+ * unwritten.
  *
  * Errors: as for fa_fwd / fa_bwd, plus FA_ERR_SHAPE when H is not a multiple
- * of H_kv and FA_ERR_WINDOW for a window bound below -1.
+ * of H_kv or S_q, S_k is negative, and FA_ERR_WINDOW for a window bound below
+ * -1.  Pointers of a side with no rows (S_q = 0 or S_k = 0) may be NULL.
  */
 int fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse,
-              int64_t B, int64_t H, int64_t H_kv, int64_t S, int64_t D,
+              int64_t B, int64_t H, int64_t H_kv, int64_t S_q, int64_t S_k, int64_t D,
               int causal, int64_t window_left, int64_t window_right,
               float scale, int dtype, void *stream);
 int fa_bwd_ex(const void *q, const void *k, const void *v, const void *o, const void *dout,
               const float *lse, void *dq, void *dk, void *dv, float *delta,
-              int64_t B, int64_t H, int64_t H_kv, int64_t S, int64_t D,
+              int64_t B, int64_t H, int64_t H_kv, int64_t S_q, int64_t S_k, int64_t D,
               int causal, int64_t window_left, int64_t window_right,
               float scale, int dtype, void *stream);
 

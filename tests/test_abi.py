@@ -181,21 +181,23 @@ def test_bwd_inputs_may_alias(fa):
     assert bcall(fa, k=P, v=P, o=P, dout=P, delta=0) == fa.FA_ERR_NULL_POINTER
 
 
-# ---- fa_fwd_ex / fa_bwd_ex: grouped heads and windows
+# ---- fa_fwd_ex / fa_bwd_ex: grouped heads, query and key lengths, windows
 XARGS = dict(ARGS, Hkv=1, wl=-1, wr=-1)
 
 
 def xcall(fa, **over):
     a = dict(XARGS, **over)
-    return fa.fa_fwd_ex(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Hkv"], a["S"], a["D"],
+    sq, sk = a.get("Sq", a["S"]), a.get("Sk", a["S"])
+    return fa.fa_fwd_ex(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Hkv"], sq, sk, a["D"],
                         a["causal"], a["wl"], a["wr"], a["scale"], a["dtype"], a["stream"])
 
 
 def xbcall(fa, **over):
     a = dict(BARGS, Hkv=1, wl=-1, wr=-1)
     a.update(over)
+    sq, sk = a.get("Sq", a["S"]), a.get("Sk", a["S"])
     return fa.fa_bwd_ex(a["q"], a["k"], a["v"], a["o"], a["dout"], a["lse"], a["dq"], a["dk"], a["dv"],
-                        a["delta"], a["B"], a["H"], a["Hkv"], a["S"], a["D"], a["causal"], a["wl"], a["wr"],
+                        a["delta"], a["B"], a["H"], a["Hkv"], sq, sk, a["D"], a["causal"], a["wl"], a["wr"],
                         a["scale"], a["dtype"], a["stream"])
 
 
@@ -225,3 +227,32 @@ def test_ex_defaults_reach_the_plain_checks(fa):
 @pytest.mark.parametrize("over", [dict(B=0), dict(S=0)])
 def test_ex_empty_problem_is_a_no_op(fa, over):
     assert xcall(fa, q=0, k=0, v=0, o=0, lse=0, wl=5, **over) == fa.FA_OK
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(Sq=-1), "FA_ERR_SHAPE"),
+    (dict(Sk=-3), "FA_ERR_SHAPE"),
+    (dict(Sq=64, Sk=256, k=0), "FA_ERR_NULL_POINTER"),   # keys exist: k is needed
+    (dict(Sq=256, Sk=64, v=0), "FA_ERR_NULL_POINTER"),
+    (dict(Sq=64, Sk=1 << 24, D=128), "FA_ERR_TOO_LARGE"),  # one head's K: S_k * D * 2 bytes >= 2^31
+])
+def test_ex_query_and_key_lengths_checked(fa, over, code):
+    # (only rejected calls: an accepted one would launch on these fake pointers)
+    assert xcall(fa, **over) == _defines()[code]
+
+
+def test_ex_rectangular_alias_uses_both_lengths(fa):
+    # q, o: B*H*Sq*D*2 = 1*4*64*64*2 = 32 KiB; k, v: B*Hkv*Sk*D*2 = 1*1*1024*64*2 = 128 KiB
+    base = dict(B=1, H=4, Hkv=1, Sq=64, Sk=1024, D=64, dtype=1)
+    q, k, v, o, lse = P, 2 * P, 3 * P, 4 * P, 5 * P
+    assert xcall(fa, q=q, k=k, v=v, o=k + 96 * 1024, lse=lse, **base) == fa.FA_ERR_ALIAS  # inside k's 128 KiB
+    assert xcall(fa, q=q, k=k, v=v, o=o, lse=q + 16 * 1024, **base) == fa.FA_ERR_ALIAS  # lse inside q
+    assert xbcall(fa, dk=v + 120 * 1024, Sq=64, Sk=1024, H=4) == fa.FA_ERR_ALIAS  # dk inside v's 128 KiB
+
+
+def test_ex_no_query_rows_is_a_no_op_forward(fa):
+    # S_q = 0: the forward has no row to write (pointers may be NULL)
+    assert xcall(fa, q=0, k=0, v=0, o=0, lse=0, Sq=0, Sk=512) == fa.FA_OK
+    assert xbcall(fa, q=0, k=0, v=0, o=0, dout=0, lse=0, dq=0, dk=0, dv=0, delta=0, Sq=0, Sk=0) == fa.FA_OK
+    # the backward still owes dK = dV = 0 for the keys
+    assert xbcall(fa, q=0, o=0, dout=0, lse=0, dq=0, delta=0, dk=0, Sq=0, Sk=512) == fa.FA_ERR_NULL_POINTER
