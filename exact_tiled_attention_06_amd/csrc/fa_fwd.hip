@@ -18,6 +18,7 @@
 #include "fa_split.hpp"
 #include "fa_bwd.hpp"
 #include "fa_window.hpp"
+#include "fa_split_window.hpp"
 
 #ifndef FA_SPLIT_TBN
 #define FA_SPLIT_TBN 128
@@ -118,17 +119,25 @@ int launch_ksplit(const Fwd& a) {
     return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
-// Sliding windows: 4 waves of 32 query rows, one 32-key tile per barrier.
+// Sliding windows: at D = 32 and 64 the two-block kernel (4 waves of 2 x 32
+// query rows), else the plain loop (4 waves of 32 rows); one 32-key tile per
+// barrier either way.
 template <typename T, int D, bool CAUSAL>
 int launch_window(const Fwd& a) {
-    using Cfg = MfmaConfig<D, CAUSAL, 1, 4, 32, false, 2, 32>;
+    using Cfg = std::conditional_t<(D == 32 || D == 64), MfmaConfig<D, CAUSAL, 2, 4, 32, true, 2, 32>,
+                                   MfmaConfig<D, CAUSAL, 1, 4, 32, false, 2, 32>>;
     const int n_qblk = (a.Sq + Cfg::BM - 1) / Cfg::BM;
     const int64_t grid = (int64_t)n_qblk * a.BH;
     if (grid > (int64_t)1 << 24) return FA_ERR_TOO_LARGE;
     (void)hipGetLastError();
-    hipLaunchKernelGGL((fa_fwd_window_kernel<T, Cfg>), dim3((unsigned)grid), dim3(Cfg::NT), 0, a.stream,
-                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse,
-                       a.Sq, a.Sk, a.BH, n_qblk, a.G, a.wl, a.wr, a.c);
+    if constexpr (D == 32 || D == 64)
+        hipLaunchKernelGGL((fa_fwd_split_window_kernel<T, Cfg>), dim3((unsigned)grid), dim3(Cfg::NT), 0, a.stream,
+                           (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse,
+                           a.Sq, a.Sk, a.BH, n_qblk, a.G, a.wl, a.wr, a.c);
+    else
+        hipLaunchKernelGGL((fa_fwd_window_kernel<T, Cfg>), dim3((unsigned)grid), dim3(Cfg::NT), 0, a.stream,
+                           (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse,
+                           a.Sq, a.Sk, a.BH, n_qblk, a.G, a.wl, a.wr, a.c);
     return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
