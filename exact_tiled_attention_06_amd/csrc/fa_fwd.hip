@@ -149,12 +149,19 @@ int launch_mfma(const Fwd& a) {
     using Small = MfmaConfig<D, CAUSAL, TL::SMALL_QB, TL::SMALL_NW, TL::SMALL_BN, TL::SMALL_PIPE>;
     const int64_t large_grid = (int64_t)((a.Sq + Large::BM - 1) / Large::BM) * a.BH;
     if (large_grid >= kFullGrid) return launch_cfg<T, Large>(a);
+    // Thinner grids split each query block's keys over the 4 waves of its
+    // workgroup.  Measured on the B=8 H=1 sweep: at D <= 64 blocks of 64 rows
+    // (two per wave) unless even those give fewer than 256 workgroups, then
+    // 32; at D = 128 blocks of 32 rows while 64-row blocks would give at most
+    // kFullGrid workgroups, else the 64-row plain kernel.
+    const int64_t grid64 = (int64_t)((a.Sq + 63) / 64) * a.BH;
     if constexpr (D <= 64) {
-        // 64 query rows per workgroup, keys split over 4 waves
-        using KSplit = MfmaConfig<D, CAUSAL, 2, 4, 32>;
-        return launch_ksplit<T, KSplit>(a);
+        if (grid64 < kFullGrid / 2) return launch_ksplit<T, MfmaConfig<D, CAUSAL, 1, 4, 32>>(a);
+        return launch_ksplit<T, MfmaConfig<D, CAUSAL, 2, 4, 32>>(a);
+    } else {
+        if (grid64 <= kFullGrid) return launch_ksplit<T, MfmaConfig<D, CAUSAL, 1, 4, 32>>(a);
+        return launch_cfg<T, Small>(a);
     }
-    return launch_cfg<T, Small>(a);
 }
 
 template <int D, bool CAUSAL>
