@@ -28,7 +28,8 @@ Prints one JSON line.  Also reported:
 Options: --gpus N (only 1 is supported: the kernel runs on one GPU),
 --steps K (timed launches), --warmup W, --workload NAME, --no-cpu-baseline,
 --sweep FILE (also time every named workload and write one JSON line per
-workload to FILE).
+workload to FILE; sweep kernels are timed from a HIP graph of 20 launches
+replayed 10 times, so short kernels carry no host launch overhead).
 """
 from __future__ import annotations
 
@@ -103,6 +104,42 @@ def time_workload(fa, torch, w, causal, steps, warmup):
     wall = time.perf_counter() - t0
     kernel_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     return wall, kernel_ms
+
+
+def time_graph(fa, torch, w, causal, launches=20, reps=10):
+    """Kernel time per launch from a HIP graph of `launches` fa_fwd_ex calls on
+    preallocated buffers, replayed `reps` times between two events: the GPU
+    never waits for the host, so short kernels are timed without the Python
+    call's overhead.  Returns the milliseconds per launch."""
+    import workloads
+    q, k, v = (x.to("cuda:0") for x in workloads.workload_inputs(w))
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.S), dtype=torch.float32, device="cuda:0")
+    wl, wr = w.window
+    code = fa.DTYPE_CODES[q.dtype]
+
+    def call(stream):
+        return fa.fa_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), w.B, w.H,
+                            k.shape[1], w.S, w.S, w.D, int(causal), wl, wr, w.scale, code, stream)
+
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        for _ in range(3):
+            fa.check(call(side.cuda_stream))
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        for _ in range(launches):
+            fa.check(call(side.cuda_stream))
+    graph.replay()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(reps):
+        graph.replay()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / (launches * reps)
 
 
 def time_backward(fa, torch, w, causal, steps, warmup):
@@ -305,8 +342,7 @@ def main():
         with open(args.sweep, "w") as f:
             for sw in workloads.ALL:
                 for c in sw.causal:
-                    wl, kms = time_workload(fa, torch, sw, c, max(10, args.steps // 4), 5)
-                    avg = sum(kms) / len(kms)
+                    avg = time_graph(fa, torch, sw, c)
                     rec = {"workload": sw.name, "causal": c, "dtype": sw.dtype, "B": sw.B, "H": sw.H,
                            "S": sw.S, "D": sw.D, "kernel_ms_avg": avg,
                            "tflops": sw.flops(c) / (avg * 1e-3) / 1e12,
