@@ -37,7 +37,7 @@
 
 namespace fa {
 
-template <int D_, bool CAUSAL_, int NW_>
+template <int D_, bool CAUSAL_, int NW_, int QBQ_ = (D_ == 128 ? 1 : 2)>
 struct BwdConfig {
     using L = MfmaConfig<D_, CAUSAL_, 1, NW_, 32>;  // staging of 32-row tiles, fragment offsets
     static constexpr int D = D_, NW = NW_;
@@ -46,8 +46,10 @@ struct BwdConfig {
     static constexpr int NT = 64 * NW;
     static constexpr int BM = 32 * NW;  // keys per dK/dV workgroup
     // dQ kernel: 32-query blocks per wave (two halve its LDS reads per MFMA;
-    // D = 128 has no registers for a second set) and queries per workgroup
-    static constexpr int QBQ = D == 128 ? 1 : 2;
+    // D = 128 has no registers for a second set; one doubles the waves of a
+    // thin grid) and queries per workgroup
+    static constexpr int QBQ = QBQ_;
+    static_assert(QBQ == 1 || (QBQ == 2 && D <= 64), "query blocks per dQ wave");
     static constexpr int BMQ = 32 * QBQ * NW;
     // D = 128 keeps two accumulators of 64 registers each in the dK/dV kernel
     static constexpr int OCC_DQ = 2;
@@ -270,7 +272,11 @@ void fa_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict
 #pragma unroll
             for (int a = 0; a < QB; ++a) {
                 st[a] = mfma32x32x16<T>(kfr, qf[a][ks], ks == 0 ? zero : st[a]);
-                dpt[a] = mfma32x32x16<T>(vfr, df[a][ks], ks == 0 ? zero : dpt[a]);
+                // the dP^T chain starts from -D, so that it ends at dP^T - D
+                f32x16 nd;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) nd[r] = -delta[a];
+                dpt[a] = mfma32x32x16<T>(vfr, df[a][ks], ks == 0 ? nd : dpt[a]);
             }
         }
         u32x4 dsp[QB][2];
@@ -289,7 +295,7 @@ void fa_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict
             for (int i = 0; i < 8; ++i) {
                 const float p0 = exp2_fast(__builtin_fmaf(st[a][2 * i], c, -lse2[a]));
                 const float p1 = exp2_fast(__builtin_fmaf(st[a][2 * i + 1], c, -lse2[a]));
-                dsp[a][i >> 2][i & 3] = pack2<T>(p0 * (dpt[a][2 * i] - delta[a]), p1 * (dpt[a][2 * i + 1] - delta[a]));
+                dsp[a][i >> 2][i & 3] = pack2<T>(p0 * dpt[a][2 * i], p1 * dpt[a][2 * i + 1]);
             }
         }
 #pragma unroll

@@ -53,6 +53,8 @@ struct Tiles {
 
 // A grid of at least this many workgroups fills the machine twice over.
 constexpr int64_t kFullGrid = 512;
+// compute units of the GPU (one workgroup each)
+constexpr int64_t kCUs = 256;
 
 int64_t elem_size(int dtype) { return dtype == FA_DTYPE_F32 ? 4 : 2; }
 
@@ -208,25 +210,43 @@ struct Bwd {
     hipStream_t stream;
 };
 
-template <typename T, int D, bool CAUSAL>
-int launch_bwd(const Bwd& a) {
-    using Cfg = BwdConfig<D, CAUSAL, 4>;
-    const int n_blk = (a.Sk + Cfg::BM - 1) / Cfg::BM;     // key blocks (dK/dV kernel)
-    const int n_qblk = (a.Sq + Cfg::BMQ - 1) / Cfg::BMQ;  // query blocks (dQ kernel)
-    if ((int64_t)n_blk * a.BH > (int64_t)1 << 24 || (int64_t)n_qblk * a.BH > (int64_t)1 << 24) return FA_ERR_TOO_LARGE;
-    const int BHkv = a.BH / a.G;
+// dQ (and D = rowsum(dO o O) into `delta`), then dK and dV, which read D
+template <typename T, typename Cfg>
+int launch_dq(const Bwd& a) {
+    const int n_qblk = (a.Sq + Cfg::BMQ - 1) / Cfg::BMQ;  // query blocks
+    if ((int64_t)n_qblk * a.BH > (int64_t)1 << 24) return FA_ERR_TOO_LARGE;
     (void)hipGetLastError();
-    // dQ (and D = rowsum(dO o O) into `delta`), then dK and dV, which read D
     hipLaunchKernelGGL((fa_bwd_dq_kernel<T, Cfg>), dim3((unsigned)((int64_t)n_qblk * a.BH)), dim3(Cfg::NT), 0,
                        a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                        (const uint16_t*)a.o, (const uint16_t*)a.dout, a.lse, (uint16_t*)a.dq, a.delta, a.Sq, a.Sk,
                        a.BH, n_qblk, a.G, a.wl, a.wr, a.c, a.scale);
-    if (hipGetLastError() != hipSuccess) return FA_ERR_LAUNCH;
+    return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+template <typename T, typename Cfg>
+int launch_dkdv(const Bwd& a) {
+    const int n_blk = (a.Sk + Cfg::BM - 1) / Cfg::BM;  // key blocks
+    const int BHkv = a.BH / a.G;
+    if ((int64_t)n_blk * BHkv > (int64_t)1 << 24) return FA_ERR_TOO_LARGE;
+    (void)hipGetLastError();
     hipLaunchKernelGGL((fa_bwd_dkdv_kernel<T, Cfg>), dim3((unsigned)((int64_t)n_blk * BHkv)), dim3(Cfg::NT), 0,
                        a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                        (const uint16_t*)a.dout, a.lse, (const float*)a.delta, (uint16_t*)a.dk, (uint16_t*)a.dv, a.Sq,
                        a.Sk, BHkv, n_blk, a.G, a.wl, a.wr, a.c, a.scale);
     return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+template <typename T, int D, bool CAUSAL>
+int launch_bwd(const Bwd& a) {
+    // dQ kernel: two 32-query blocks per wave (D <= 64), unless that leaves
+    // fewer workgroups than CUs; then one block per wave, twice the waves
+    using Q2 = BwdConfig<D, CAUSAL, 4>;
+    using Q1 = BwdConfig<D, CAUSAL, 4, 1>;
+    using KV = BwdConfig<D, CAUSAL, 4>;
+    const int64_t grid_q2 = (int64_t)((a.Sq + Q2::BMQ - 1) / Q2::BMQ) * a.BH;
+    const int r = (D > 64 || grid_q2 >= kCUs) ? launch_dq<T, Q2>(a) : launch_dq<T, Q1>(a);
+    if (r != FA_OK) return r;
+    return launch_dkdv<T, KV>(a);
 }
 
 template <bool CAUSAL>
