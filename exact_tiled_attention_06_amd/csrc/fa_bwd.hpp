@@ -37,13 +37,18 @@
 
 namespace fa {
 
-template <int D_, bool CAUSAL_, int NW_, int QBQ_ = (D_ == 128 ? 1 : 2)>
+template <int D_, bool CAUSAL_, int NW_, int QBQ_ = (D_ == 128 ? 1 : 2), int QS_ = 1>
 struct BwdConfig {
     using L = MfmaConfig<D_, CAUSAL_, 1, NW_, 32>;  // staging of 32-row tiles, fragment offsets
     static constexpr int D = D_, NW = NW_;
     static constexpr bool CAUSAL = CAUSAL_;
     static constexpr int KS = L::KS, DB = L::DB, RB = L::RB, TILE = L::TILE;
     static constexpr int NT = 64 * NW;
+    // dK/dV kernel: QS groups of NW waves share a key block and split its
+    // query steps (QS = 2 doubles the waves of a thin grid)
+    static constexpr int QS = QS_;
+    static constexpr int NT_KV = 64 * NW * QS;
+    static_assert(QS == 1 || (QS == 2 && (D == 32 || D == 64)), "query split of the dK/dV kernel");
     static constexpr int BM = 32 * NW;  // keys per dK/dV workgroup
     // dQ kernel: 32-query blocks per wave (two halve its LDS reads per MFMA;
     // D = 128 has no registers for a second set; one doubles the waves of a
@@ -322,7 +327,8 @@ void fa_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict
 // ---------------------------------------------------------------- dK/dV kernel
 
 template <typename T, typename Cfg>
-__global__ __attribute__((amdgpu_flat_work_group_size(Cfg::NT, Cfg::NT), amdgpu_waves_per_eu(Cfg::OCC_KV, Cfg::OCC_KV)))
+__global__ __attribute__((amdgpu_flat_work_group_size(Cfg::NT_KV, Cfg::NT_KV),
+                          amdgpu_waves_per_eu(Cfg::OCC_KV, Cfg::OCC_KV)))
 void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                         const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
                         const float* __restrict__ LSE, const float* __restrict__ DELTA,
@@ -333,38 +339,46 @@ void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
     constexpr int D = Cfg::D, KS = Cfg::KS, DB = Cfg::DB, RB = Cfg::RB, BM = Cfg::BM;
     constexpr bool CAUSAL = Cfg::CAUSAL;
 
+    constexpr int QS = Cfg::QS;
+
     // per Q/dO tile: Q row layout (S operand), Q transposed layout (dK^T
     // operand), dO row layout (dP operand), dO transposed layout (dV^T
     // operand), and the tile's 32 lse and D values; three buffers each, so
-    // that tiles are staged two steps ahead
-    __shared__ __attribute__((aligned(1024))) char qr0[Cfg::TILE];
-    __shared__ __attribute__((aligned(1024))) char qr1[Cfg::TILE];
-    __shared__ __attribute__((aligned(1024))) char qr2[Cfg::TILE];
-    __shared__ __attribute__((aligned(1024))) char qt0[Cfg::TILE];
-    __shared__ __attribute__((aligned(1024))) char qt1[Cfg::TILE];
-    __shared__ __attribute__((aligned(1024))) char qt2[Cfg::TILE];
-    __shared__ __attribute__((aligned(1024))) char or0[Cfg::TILE];
-    __shared__ __attribute__((aligned(1024))) char or1[Cfg::TILE];
-    __shared__ __attribute__((aligned(1024))) char or2[Cfg::TILE];
-    __shared__ __attribute__((aligned(1024))) char ot0[Cfg::TILE];
-    __shared__ __attribute__((aligned(1024))) char ot1[Cfg::TILE];
-    __shared__ __attribute__((aligned(1024))) char ot2[Cfg::TILE];
-    __shared__ __attribute__((aligned(16))) float ls0[32];
-    __shared__ __attribute__((aligned(16))) float ls1[32];
-    __shared__ __attribute__((aligned(16))) float ls2[32];
-    __shared__ __attribute__((aligned(16))) float dl0[32];
-    __shared__ __attribute__((aligned(16))) float dl1[32];
-    __shared__ __attribute__((aligned(16))) float dl2[32];
-    FA_LDS char* const qrb[3] = {(FA_LDS char*)qr0, (FA_LDS char*)qr1, (FA_LDS char*)qr2};
-    FA_LDS char* const qtb[3] = {(FA_LDS char*)qt0, (FA_LDS char*)qt1, (FA_LDS char*)qt2};
-    FA_LDS char* const orb[3] = {(FA_LDS char*)or0, (FA_LDS char*)or1, (FA_LDS char*)or2};
-    FA_LDS char* const otb[3] = {(FA_LDS char*)ot0, (FA_LDS char*)ot1, (FA_LDS char*)ot2};
-    FA_LDS float* const lsb[3] = {(FA_LDS float*)ls0, (FA_LDS float*)ls1, (FA_LDS float*)ls2};
-    FA_LDS float* const dlb[3] = {(FA_LDS float*)dl0, (FA_LDS float*)dl1, (FA_LDS float*)dl2};
+    // that tiles are staged two steps ahead; one slice of each per wave group
+    __shared__ __attribute__((aligned(1024))) char qr0[QS * Cfg::TILE];
+    __shared__ __attribute__((aligned(1024))) char qr1[QS * Cfg::TILE];
+    __shared__ __attribute__((aligned(1024))) char qr2[QS * Cfg::TILE];
+    __shared__ __attribute__((aligned(1024))) char qt0[QS * Cfg::TILE];
+    __shared__ __attribute__((aligned(1024))) char qt1[QS * Cfg::TILE];
+    __shared__ __attribute__((aligned(1024))) char qt2[QS * Cfg::TILE];
+    __shared__ __attribute__((aligned(1024))) char or0[QS * Cfg::TILE];
+    __shared__ __attribute__((aligned(1024))) char or1[QS * Cfg::TILE];
+    __shared__ __attribute__((aligned(1024))) char or2[QS * Cfg::TILE];
+    __shared__ __attribute__((aligned(1024))) char ot0[QS * Cfg::TILE];
+    __shared__ __attribute__((aligned(1024))) char ot1[QS * Cfg::TILE];
+    __shared__ __attribute__((aligned(1024))) char ot2[QS * Cfg::TILE];
+    __shared__ __attribute__((aligned(16))) float ls0[QS * 32];
+    __shared__ __attribute__((aligned(16))) float ls1[QS * 32];
+    __shared__ __attribute__((aligned(16))) float ls2[QS * 32];
+    __shared__ __attribute__((aligned(16))) float dl0[QS * 32];
+    __shared__ __attribute__((aligned(16))) float dl1[QS * 32];
+    __shared__ __attribute__((aligned(16))) float dl2[QS * 32];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // Wave group grp (of QS) walks its share of the key block's query steps;
+    // `wave` is the wave's index in its group, which fixes its keys and its
+    // share of the staging.
+    const int grp = __builtin_amdgcn_readfirstlane(tid >> 6) / Cfg::NW;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6) % Cfg::NW;
+    const int gt = grp * Cfg::TILE, gs = grp * 32;
+    FA_LDS char* const qrb[3] = {(FA_LDS char*)qr0 + gt, (FA_LDS char*)qr1 + gt, (FA_LDS char*)qr2 + gt};
+    FA_LDS char* const qtb[3] = {(FA_LDS char*)qt0 + gt, (FA_LDS char*)qt1 + gt, (FA_LDS char*)qt2 + gt};
+    FA_LDS char* const orb[3] = {(FA_LDS char*)or0 + gt, (FA_LDS char*)or1 + gt, (FA_LDS char*)or2 + gt};
+    FA_LDS char* const otb[3] = {(FA_LDS char*)ot0 + gt, (FA_LDS char*)ot1 + gt, (FA_LDS char*)ot2 + gt};
+    FA_LDS float* const lsb[3] = {(FA_LDS float*)ls0 + gs, (FA_LDS float*)ls1 + gs, (FA_LDS float*)ls2 + gs};
+    FA_LDS float* const dlb[3] = {(FA_LDS float*)dl0 + gs, (FA_LDS float*)dl1 + gs, (FA_LDS float*)dl2 + gs};
+
     const int n = lane & 31;
     const int h = lane >> 5;
 
@@ -406,12 +420,21 @@ void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
         for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int r = 0; r < 16; ++r) zero[db][r] = 0.f;
-        if (live && kw + n < Sk) {
+        if (grp == 0 && live && kw + n < Sk) {
             store_t<T, D, DB>(dK + kvhead, kw + n, h, zero, 1.0f);
             store_t<T, D, DB>(dV + kvhead, kw + n, h, zero, 1.0f);
         }
         return;
     }
+    // group grp takes steps ub .. ub + nmine - 1 (nmine may be 0 for the
+    // last group); every group runs nsh steps, the extra ones as padding
+    const int nsh = (nsteps + QS - 1) / QS;
+    const int ub = grp * nsh;
+    const int nmine = min(nsh, nsteps - ub);
+    // the step whose tiles a group stages at its local step u: clamped to
+    // the group's last real step (or, for a group without steps, to the step
+    // before its range), so every staging reads a valid tile
+    auto ug = [&](int u) { return ub + min(u, nmine - 1); };
 
     // step u: query head kvbh*G + u / nt, query tile t0 + u % nt
     auto stage = [&](auto par, int u) __attribute__((always_inline)) {
@@ -454,7 +477,6 @@ void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
     // the loop body is straight-line in its loads and one wait count holds.
     constexpr int kStepOps = 2 + 4 * L::LOADS_PER_WAVE;
     const bool stages = L::LOADS >= L::NW || wave < L::LOADS;  // wave-uniform
-    const int ulast = nsteps - 1;
 
     // resident: K and V fragments of the wave's 32 keys, loaded together with
     // the first two steps' loads; the prologue ends with all of them complete
@@ -462,10 +484,10 @@ void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
     u32x4 kf[KS], vf[KS];
     row_frags<KS>(K + kvhead, krow, D, h, kf);
     row_frags<KS>(V + kvhead, krow, D, h, vf);
-    fetch_ld(P0{}, 0);
-    stage(P0{}, 0);
-    fetch_ld(P1{}, min(1, ulast));
-    stage(P1{}, min(1, ulast));
+    fetch_ld(P0{}, ug(0));
+    stage(P0{}, ug(0));
+    fetch_ld(P1{}, ug(1));
+    stage(P1{}, ug(1));
     // (the asm operands make the compiler complete these loads here rather
     // than sink them into the loop, where their waits would land in every
     // iteration)
@@ -499,10 +521,10 @@ void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
             dlb[P][lane] = -dreg[P];
         }
         lds_barrier();
-        fetch_ld(std::integral_constant<int, (P + 2) % 3>{}, min(u + 2, ulast));
-        stage(std::integral_constant<int, (P + 2) % 3>{}, min(u + 2, ulast));
-        if (u >= nsteps) return;  // padding step
-        const int t = t0 + u % nt;
+        fetch_ld(std::integral_constant<int, (P + 2) % 3>{}, ug(u + 2));
+        stage(std::integral_constant<int, (P + 2) % 3>{}, ug(u + 2));
+        if (u >= nmine) return;  // padding step
+        const int t = t0 + (ub + u) % nt;
         if (t < tw0 || t >= tw1) return;  // wave-uniform
         // query of register r: 32t + 8(r/4) + 4h + r%4; lse and -D for the
         // four consecutive queries of each register group come in one 16-byte
@@ -564,12 +586,39 @@ void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
                 dkacc[db] = mfma32x32x16<T>(W::v_frag(qtb[P], offv, 0, j, db), dsp[j], dkacc[db]);
             }
     };
-    for (int u = 0; u < nsteps; u += 3) {
+    for (int u = 0; u < nsh; u += 3) {
         step(P0{}, u);
         step(P1{}, u + 1);
         step(P2{}, u + 2);
     }
     wait_vmcnt0();  // the spare stagings of the last steps
+
+    if constexpr (QS == 2) {
+        // group 1 hands its fp32 partial sums to group 0 through LDS (two of
+        // the staging arrays per wave, free once every wave is past the loop)
+        static_assert(Cfg::NW == 4 && DB * 16 * 64 * 4 <= QS * Cfg::TILE, "exchange fits the staging arrays");
+        __syncthreads();
+        float* const xk = (float*)(wave == 0 ? qr0 : wave == 1 ? qr1 : wave == 2 ? qr2 : qt0);
+        float* const xv = (float*)(wave == 0 ? qt1 : wave == 1 ? qt2 : wave == 2 ? or0 : or1);
+        if (grp == 1) {
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    xk[(db * 16 + r) * 64 + lane] = dkacc[db][r];
+                    xv[(db * 16 + r) * 64 + lane] = dvacc[db][r];
+                }
+        }
+        __syncthreads();
+        if (grp == 1) return;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                dkacc[db][r] += xk[(db * 16 + r) * 64 + lane];
+                dvacc[db][r] += xv[(db * 16 + r) * 64 + lane];
+            }
+    }
 
     if (live && kw + n < Sk) {
         store_t<T, D, DB>(dK + kvhead, kw + n, h, dkacc, scale);

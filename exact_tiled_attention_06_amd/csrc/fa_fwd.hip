@@ -229,7 +229,7 @@ int launch_dkdv(const Bwd& a) {
     const int BHkv = a.BH / a.G;
     if ((int64_t)n_blk * BHkv > (int64_t)1 << 24) return FA_ERR_TOO_LARGE;
     (void)hipGetLastError();
-    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<T, Cfg>), dim3((unsigned)((int64_t)n_blk * BHkv)), dim3(Cfg::NT), 0,
+    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<T, Cfg>), dim3((unsigned)((int64_t)n_blk * BHkv)), dim3(Cfg::NT_KV), 0,
                        a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                        (const uint16_t*)a.dout, a.lse, (const float*)a.delta, (uint16_t*)a.dk, (uint16_t*)a.dv, a.Sq,
                        a.Sk, BHkv, n_blk, a.G, a.wl, a.wr, a.c, a.scale);
@@ -242,11 +242,16 @@ int launch_bwd(const Bwd& a) {
     // fewer workgroups than CUs; then one block per wave, twice the waves
     using Q2 = BwdConfig<D, CAUSAL, 4>;
     using Q1 = BwdConfig<D, CAUSAL, 4, 1>;
-    using KV = BwdConfig<D, CAUSAL, 4>;
     const int64_t grid_q2 = (int64_t)((a.Sq + Q2::BMQ - 1) / Q2::BMQ) * a.BH;
     const int r = (D > 64 || grid_q2 >= kCUs) ? launch_dq<T, Q2>(a) : launch_dq<T, Q1>(a);
     if (r != FA_OK) return r;
-    return launch_dkdv<T, KV>(a);
+    // dK/dV kernel: a wave owns 32 keys whatever the workgroup, so a grid of
+    // fewer than two workgroups per CU splits each key block's query steps
+    // over two groups of 4 waves (D = 32, 64)
+    using KV = BwdConfig<D, CAUSAL, 4>;
+    using KV2 = BwdConfig<D, CAUSAL, 4, Q2::QBQ, (D == 32 || D == 64) ? 2 : 1>;
+    const int64_t grid_kv = (int64_t)((a.Sk + KV::BM - 1) / KV::BM) * (a.BH / a.G);
+    return grid_kv >= kFullGrid ? launch_dkdv<T, KV>(a) : launch_dkdv<T, KV2>(a);
 }
 
 template <bool CAUSAL>
