@@ -37,7 +37,7 @@
 
 namespace fa {
 
-template <int D_, bool CAUSAL_, int NW_, int QBQ_ = (D_ == 128 ? 1 : 2), int QS_ = 1>
+template <int D_, bool CAUSAL_, int NW_, int QBQ_ = (D_ == 128 ? 1 : 2), int QS_ = 1, int KSQ_ = 1>
 struct BwdConfig {
     using L = MfmaConfig<D_, CAUSAL_, 1, NW_, 32>;  // staging of 32-row tiles, fragment offsets
     static constexpr int D = D_, NW = NW_;
@@ -49,6 +49,11 @@ struct BwdConfig {
     static constexpr int QS = QS_;
     static constexpr int NT_KV = 64 * NW * QS;
     static_assert(QS == 1 || (QS == 2 && (D == 32 || D == 64)), "query split of the dK/dV kernel");
+    // dQ kernel: KSQ groups of NW waves share a query block and split its
+    // key tiles (KSQ = 2 doubles the waves of a thin grid)
+    static constexpr int KSQ = KSQ_;
+    static constexpr int NT_Q = 64 * NW * KSQ;
+    static_assert(KSQ == 1 || (KSQ == 2 && QBQ_ == 1 && (D == 32 || D == 64)), "key split of the dQ kernel");
     static constexpr int BM = 32 * NW;  // keys per dK/dV workgroup
     // dQ kernel: 32-query blocks per wave (two halve its LDS reads per MFMA;
     // D = 128 has no registers for a second set; one doubles the waves of a
@@ -141,7 +146,7 @@ __device__ __forceinline__ void store_t(uint16_t* xh, int row, int h, const f32x
 // ------------------------------------------------------------------ dQ kernel
 
 template <typename T, typename Cfg>
-__global__ __attribute__((amdgpu_flat_work_group_size(Cfg::NT, Cfg::NT), amdgpu_waves_per_eu(Cfg::OCC_DQ, Cfg::OCC_DQ)))
+__global__ __attribute__((amdgpu_flat_work_group_size(Cfg::NT_Q, Cfg::NT_Q), amdgpu_waves_per_eu(Cfg::OCC_DQ, Cfg::OCC_DQ)))
 void fa_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                       const uint16_t* __restrict__ V, const uint16_t* __restrict__ O,
                       const uint16_t* __restrict__ dO, const float* __restrict__ LSE,
@@ -152,21 +157,29 @@ void fa_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict
     constexpr int D = Cfg::D, KS = Cfg::KS, DB = Cfg::DB, RB = Cfg::RB;
     constexpr bool CAUSAL = Cfg::CAUSAL;
 
+    constexpr int KSQ = Cfg::KSQ;
+
     // per K/V tile: K row layout (S^T operand), K transposed layout (dQ^T
-    // operand), V row layout (dP^T operand); two buffers each
-    __shared__ __attribute__((aligned(1024))) char kr0[Cfg::TILE];
-    __shared__ __attribute__((aligned(1024))) char kr1[Cfg::TILE];
-    __shared__ __attribute__((aligned(1024))) char kt0[Cfg::TILE];
-    __shared__ __attribute__((aligned(1024))) char kt1[Cfg::TILE];
-    __shared__ __attribute__((aligned(1024))) char vr0[Cfg::TILE];
-    __shared__ __attribute__((aligned(1024))) char vr1[Cfg::TILE];
-    FA_LDS char* const krb[2] = {(FA_LDS char*)kr0, (FA_LDS char*)kr1};
-    FA_LDS char* const ktb[2] = {(FA_LDS char*)kt0, (FA_LDS char*)kt1};
-    FA_LDS char* const vrb[2] = {(FA_LDS char*)vr0, (FA_LDS char*)vr1};
+    // operand), V row layout (dP^T operand); two buffers each, one slice of
+    // each per wave group
+    __shared__ __attribute__((aligned(1024))) char kr0[KSQ * Cfg::TILE];
+    __shared__ __attribute__((aligned(1024))) char kr1[KSQ * Cfg::TILE];
+    __shared__ __attribute__((aligned(1024))) char kt0[KSQ * Cfg::TILE];
+    __shared__ __attribute__((aligned(1024))) char kt1[KSQ * Cfg::TILE];
+    __shared__ __attribute__((aligned(1024))) char vr0[KSQ * Cfg::TILE];
+    __shared__ __attribute__((aligned(1024))) char vr1[KSQ * Cfg::TILE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // Wave group grp (of KSQ) walks its share of the query block's key tiles;
+    // `wave` is the wave's index in its group, which fixes its queries and
+    // its share of the staging.
+    const int grp = KSQ == 1 ? 0 : __builtin_amdgcn_readfirstlane(tid >> 6) / Cfg::NW;
+    const int wave = KSQ == 1 ? __builtin_amdgcn_readfirstlane(tid >> 6) : __builtin_amdgcn_readfirstlane(tid >> 6) % Cfg::NW;
+    const int gt = grp * Cfg::TILE;
+    FA_LDS char* const krb[2] = {(FA_LDS char*)kr0 + gt, (FA_LDS char*)kr1 + gt};
+    FA_LDS char* const ktb[2] = {(FA_LDS char*)kt0 + gt, (FA_LDS char*)kt1 + gt};
+    FA_LDS char* const vrb[2] = {(FA_LDS char*)vr0 + gt, (FA_LDS char*)vr1 + gt};
     const int n = lane & 31;
     const int h = lane >> 5;
 
@@ -195,6 +208,11 @@ void fa_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict
     const int qlast = min(q0 + BMQ, Sq) - 1;
     const int tb = lo_of(q0) / 32;                 // the workgroup's key tiles [tb, te)
     const int te = hi_of(qlast) / 32 + 1;
+    // group grp takes tiles [tgb, tge); every group runs nth steps, a group
+    // with fewer tiles as padding (staging nothing, computing nothing)
+    const int nth = KSQ == 1 ? te - tb : max(0, (te - tb + KSQ - 1) / KSQ);
+    const int tgb = KSQ == 1 ? tb : tb + grp * nth;
+    const int tge = KSQ == 1 ? te : min(te, tgb + nth);
     // per block a: tiles in [ml, mu) need no mask; the wave computes tiles
     // [wb, we), the union over its blocks (a block masks the tiles outside its
     // own range entirely)
@@ -235,7 +253,7 @@ void fa_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict
         row_frags<KS>(O + head, qrow[a], D, h, of[a]);
     }
     issue_order();
-    stage(P0{}, tb);
+    if (KSQ == 1 || tgb < tge) stage(P0{}, tgb);
     float delta[QB], lse2[QB];
 #pragma unroll
     for (int a = 0; a < QB; ++a) {
@@ -245,7 +263,7 @@ void fa_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) part += dot8<T>(df[a][ks], of[a][ks]);
         delta[a] = halves_sum(part);
-        if (h == 0 && qw + 32 * a + n < Sq) DELTA[(int64_t)bh * Sq + qw + 32 * a + n] = delta[a];
+        if (grp == 0 && h == 0 && qw + 32 * a + n < Sq) DELTA[(int64_t)bh * Sq + qw + 32 * a + n] = delta[a];
         // a row with no key (lse = -inf; all its scores are masked to -inf)
         // takes +inf, so that its masked scores give exp2(-inf) = 0
         lse2[a] = first[a] <= last[a] ? LSE[(int64_t)bh * Sq + qrow[a]] * kLog2e : __builtin_inff();
@@ -266,8 +284,8 @@ void fa_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict
         constexpr int P = decltype(par)::value;
         wait_vmcnt0();
         __syncthreads();
-        if (t + 1 < te) stage(std::integral_constant<int, 1 - P>{}, t + 1);
-        if (t < wb || t >= we) return;  // wave-uniform
+        if (t + 1 < tge) stage(std::integral_constant<int, 1 - P>{}, t + 1);
+        if ((KSQ > 1 && t >= tge) || t < wb || t >= we) return;  // wave-uniform
         const f32x16 zero = {};
         f32x16 st[QB], dpt[QB];
 #pragma unroll
@@ -312,12 +330,33 @@ void fa_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict
                 for (int a = 0; a < QB; ++a) dqacc[a][db] = mfma32x32x16<T>(ktf, dsp[a][j], dqacc[a][db]);
             }
     };
-    int t = tb;
-    for (; t + 1 < te; t += 2) {
-        step(P0{}, t);
-        step(P1{}, t + 1);
+    int i = 0;
+    for (; i + 1 < nth; i += 2) {
+        step(P0{}, tgb + i);
+        step(P1{}, tgb + i + 1);
     }
-    if (t < te) step(P0{}, t);
+    if (i < nth) step(P0{}, tgb + i);
+
+    if constexpr (KSQ == 2) {
+        // group 1 hands its fp32 partial dQ to group 0 through LDS (one
+        // staging array per wave, free once every wave is past the loop)
+        static_assert(Cfg::NW == 4 && QB == 1 && DB * 16 * 64 * 4 <= KSQ * Cfg::TILE, "exchange fits");
+        wait_vmcnt0();
+        __syncthreads();
+        float* const x = (float*)(wave == 0 ? kr0 : wave == 1 ? kr1 : wave == 2 ? kt0 : kt1);
+        if (grp == 1) {
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) x[(db * 16 + r) * 64 + lane] = dqacc[0][db][r];
+        }
+        __syncthreads();
+        if (grp == 1) return;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) dqacc[0][db][r] += x[(db * 16 + r) * 64 + lane];
+    }
 
 #pragma unroll
     for (int a = 0; a < QB; ++a)
@@ -369,8 +408,8 @@ void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
     // Wave group grp (of QS) walks its share of the key block's query steps;
     // `wave` is the wave's index in its group, which fixes its keys and its
     // share of the staging.
-    const int grp = __builtin_amdgcn_readfirstlane(tid >> 6) / Cfg::NW;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6) % Cfg::NW;
+    const int grp = QS == 1 ? 0 : __builtin_amdgcn_readfirstlane(tid >> 6) / Cfg::NW;
+    const int wave = QS == 1 ? __builtin_amdgcn_readfirstlane(tid >> 6) : __builtin_amdgcn_readfirstlane(tid >> 6) % Cfg::NW;
     const int gt = grp * Cfg::TILE, gs = grp * 32;
     FA_LDS char* const qrb[3] = {(FA_LDS char*)qr0 + gt, (FA_LDS char*)qr1 + gt, (FA_LDS char*)qr2 + gt};
     FA_LDS char* const qtb[3] = {(FA_LDS char*)qt0 + gt, (FA_LDS char*)qt1 + gt, (FA_LDS char*)qt2 + gt};

@@ -216,7 +216,7 @@ int launch_dq(const Bwd& a) {
     const int n_qblk = (a.Sq + Cfg::BMQ - 1) / Cfg::BMQ;  // query blocks
     if ((int64_t)n_qblk * a.BH > (int64_t)1 << 24) return FA_ERR_TOO_LARGE;
     (void)hipGetLastError();
-    hipLaunchKernelGGL((fa_bwd_dq_kernel<T, Cfg>), dim3((unsigned)((int64_t)n_qblk * a.BH)), dim3(Cfg::NT), 0,
+    hipLaunchKernelGGL((fa_bwd_dq_kernel<T, Cfg>), dim3((unsigned)((int64_t)n_qblk * a.BH)), dim3(Cfg::NT_Q), 0,
                        a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                        (const uint16_t*)a.o, (const uint16_t*)a.dout, a.lse, (uint16_t*)a.dq, a.delta, a.Sq, a.Sk,
                        a.BH, n_qblk, a.G, a.wl, a.wr, a.c, a.scale);
@@ -239,11 +239,17 @@ int launch_dkdv(const Bwd& a) {
 template <typename T, int D, bool CAUSAL>
 int launch_bwd(const Bwd& a) {
     // dQ kernel: two 32-query blocks per wave (D <= 64), unless that leaves
-    // fewer workgroups than CUs; then one block per wave, twice the waves
+    // fewer workgroups than CUs; then one block per wave, twice the waves,
+    // and if that still leaves fewer than two workgroups per CU, two groups
+    // of 4 waves per query block that split its key tiles (D = 32, 64)
     using Q2 = BwdConfig<D, CAUSAL, 4>;
     using Q1 = BwdConfig<D, CAUSAL, 4, 1>;
+    using Q1K = BwdConfig<D, CAUSAL, 4, 1, 1, (D == 32 || D == 64) ? 2 : 1>;
     const int64_t grid_q2 = (int64_t)((a.Sq + Q2::BMQ - 1) / Q2::BMQ) * a.BH;
-    const int r = (D > 64 || grid_q2 >= kCUs) ? launch_dq<T, Q2>(a) : launch_dq<T, Q1>(a);
+    const int64_t grid_q1 = (int64_t)((a.Sq + Q1::BMQ - 1) / Q1::BMQ) * a.BH;
+    const int r = (D > 64 || grid_q2 >= kCUs) ? launch_dq<T, Q2>(a)
+                  : grid_q1 >= kFullGrid      ? launch_dq<T, Q1>(a)
+                                              : launch_dq<T, Q1K>(a);
     if (r != FA_OK) return r;
     // dK/dV kernel: a wave owns 32 keys whatever the workgroup, so a grid of
     // fewer than two workgroups per CU splits each key block's query steps
