@@ -132,22 +132,6 @@ __device__ __forceinline__ void wait_vmcnt() {
 // the compiler from moving memory accesses across it.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// Wait until at most n (0..8, wave-uniform) of this wave's vector-memory
-// operations are outstanding; s_waitcnt takes the count as an immediate.
-__device__ __forceinline__ void wait_vmcnt_le(int n) {
-    switch (n) {
-        case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
-        case 1: __builtin_amdgcn_s_waitcnt(0x0F71); break;
-        case 2: __builtin_amdgcn_s_waitcnt(0x0F72); break;
-        case 3: __builtin_amdgcn_s_waitcnt(0x0F73); break;
-        case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
-        case 5: __builtin_amdgcn_s_waitcnt(0x0F75); break;
-        case 6: __builtin_amdgcn_s_waitcnt(0x0F76); break;
-        case 7: __builtin_amdgcn_s_waitcnt(0x0F77); break;
-        default: __builtin_amdgcn_s_waitcnt(0x0F78); break;
-    }
-}
-
 // Per-lane byte offset (within one head's K or V) of this wave's i-th 16-byte
 // transfer of a tile starting at key 0: transfer `inst` of the tile covers LDS
 // bytes inst*1024 .. +1023, lane l fills 16 bytes at l*16 of it, i.e. row
