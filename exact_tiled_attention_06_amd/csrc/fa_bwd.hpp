@@ -53,7 +53,7 @@ struct BwdConfig {
     // key tiles (KSQ = 2 doubles the waves of a thin grid)
     static constexpr int KSQ = KSQ_;
     static constexpr int NT_Q = 64 * NW * KSQ;
-    static_assert(KSQ == 1 || (KSQ == 2 && QBQ_ == 1 && (D == 32 || D == 64)), "key split of the dQ kernel");
+    static_assert(KSQ == 1 || (KSQ == 2 && QBQ_ == 1 && D >= 32), "key split of the dQ kernel");
     static constexpr int BM = 32 * NW;  // keys per dK/dV workgroup
     // dQ kernel: 32-query blocks per wave (two halve its LDS reads per MFMA;
     // D = 128 has no registers for a second set; one doubles the waves of a

@@ -239,17 +239,18 @@ int launch_dkdv(const Bwd& a) {
 template <typename T, int D, bool CAUSAL>
 int launch_bwd(const Bwd& a) {
     // dQ kernel: two 32-query blocks per wave (D <= 64), unless that leaves
-    // fewer workgroups than CUs; then one block per wave, twice the waves,
-    // and if that still leaves fewer than two workgroups per CU, two groups
-    // of 4 waves per query block that split its key tiles (D = 32, 64)
+    // fewer workgroups than CUs; then one block per wave, twice the waves
+    // (D = 128 has one block per wave anyway), and if that still leaves
+    // fewer than two workgroups per CU, two groups of 4 waves per query block
+    // that split its key tiles (D >= 32)
     using Q2 = BwdConfig<D, CAUSAL, 4>;
     using Q1 = BwdConfig<D, CAUSAL, 4, 1>;
-    using Q1K = BwdConfig<D, CAUSAL, 4, 1, 1, (D == 32 || D == 64) ? 2 : 1>;
+    using Q1K = BwdConfig<D, CAUSAL, 4, 1, 1, D >= 32 ? 2 : 1>;
     const int64_t grid_q2 = (int64_t)((a.Sq + Q2::BMQ - 1) / Q2::BMQ) * a.BH;
     const int64_t grid_q1 = (int64_t)((a.Sq + Q1::BMQ - 1) / Q1::BMQ) * a.BH;
-    const int r = (D > 64 || grid_q2 >= kCUs) ? launch_dq<T, Q2>(a)
-                  : grid_q1 >= kFullGrid      ? launch_dq<T, Q1>(a)
-                                              : launch_dq<T, Q1K>(a);
+    const int r = (D <= 64 && grid_q2 >= kCUs) ? launch_dq<T, Q2>(a)
+                  : grid_q1 >= kFullGrid       ? launch_dq<T, Q1>(a)
+                                               : launch_dq<T, Q1K>(a);
     if (r != FA_OK) return r;
     // dK/dV kernel: a wave owns 32 keys whatever the workgroup, so a grid of
     // fewer than two workgroups per CU splits each key block's query steps
