@@ -340,7 +340,7 @@ void fa_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict
     if constexpr (KSQ == 2) {
         // group 1 hands its fp32 partial dQ to group 0 through LDS (one
         // staging array per wave, free once every wave is past the loop)
-        static_assert(Cfg::NW == 4 && QB == 1 && DB * 16 * 64 * 4 <= KSQ * Cfg::TILE, "exchange fits");
+        static_assert(Cfg::NW <= 4 && QB == 1 && DB * 16 * 64 * 4 <= KSQ * Cfg::TILE, "exchange fits");
         wait_vmcnt0();
         __syncthreads();
         float* const x = (float*)(wave == 0 ? kr0 : wave == 1 ? kr1 : wave == 2 ? kt0 : kt1);

@@ -241,11 +241,14 @@ int launch_bwd(const Bwd& a) {
     // dQ kernel: two 32-query blocks per wave (D <= 64), unless that leaves
     // fewer workgroups than CUs; then one block per wave, twice the waves
     // (D = 128 has one block per wave anyway), and if that still leaves
-    // fewer than two workgroups per CU, two groups of 4 waves per query block
-    // that split its key tiles (D >= 32)
+    // fewer than two workgroups per CU, two groups of waves per query block
+    // that split its key tiles (D >= 32): groups of 2 waves (64 rows, 4-wave
+    // workgroups, 48 KB of LDS at D = 64) at D = 32, 64, where fewer waves
+    // behind each barrier wait less; of 4 at D = 128, whose 96 KB of LDS
+    // admit one workgroup per CU
     using Q2 = BwdConfig<D, CAUSAL, 4>;
     using Q1 = BwdConfig<D, CAUSAL, 4, 1>;
-    using Q1K = BwdConfig<D, CAUSAL, 4, 1, 1, D >= 32 ? 2 : 1>;
+    using Q1K = BwdConfig<D, CAUSAL, (D == 32 || D == 64) ? 2 : 4, 1, 1, D >= 32 ? 2 : 1>;
     const int64_t grid_q2 = (int64_t)((a.Sq + Q2::BMQ - 1) / Q2::BMQ) * a.BH;
     const int64_t grid_q1 = (int64_t)((a.Sq + Q1::BMQ - 1) / Q1::BMQ) * a.BH;
     const int r = (D <= 64 && grid_q2 >= kCUs) ? launch_dq<T, Q2>(a)
