@@ -227,6 +227,9 @@ def main():
     ap.add_argument("--traffic-bytes", type=float, default=None,
                     help="HBM bytes per launch measured with rocprofv3 counters")
     ap.add_argument("--sweep", default=None, help="write per-workload JSON lines to this file")
+    ap.add_argument("--micro", default=None,
+                    help="instead of attention, run the instruction-rate microbenchmarks (libfa_micro.so) and "
+                         "write their table, one JSON line per probe, to this file")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="instead of attention, run plain device-to-device copies of this many bytes "
                          "(calibrates the FETCH_SIZE / WRITE_SIZE counters against a known byte count)")
@@ -249,6 +252,17 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         return 1
+
+    if args.micro:
+        from exact_tiled_attention_06_amd import micro
+        rows = micro.table()
+        with open(args.micro, "w") as f:
+            for r in rows:
+                f.write(json.dumps(r) + "\n")
+                print(f"micro {r['kind']:6s} {r['cycles']:8.2f}  {r['unit']}"
+                      + (f"  (vector wave {r['vector_wave_cycles']})" if "vector_wave_cycles" in r else ""),
+                      flush=True)
+        return 0
 
     if args.copy_bytes:
         n = args.copy_bytes // 4

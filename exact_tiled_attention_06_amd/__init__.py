@@ -180,8 +180,8 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = Fa
                          f"{tuple(q.shape)}, {tuple(k.shape)}, {tuple(v.shape)}")
     if not (q.dtype == k.dtype == v.dtype) or q.dtype not in DTYPE_CODES:
         raise ValueError(f"q, k, v must share one of {list(DTYPE_CODES)}; got {q.dtype}, {k.dtype}, {v.dtype}")
-    if not (q.is_cuda and k.is_cuda and v.is_cuda):
-        raise RuntimeError("q, k, v must be device tensors")
+    if not (q.is_cuda and k.is_cuda and v.is_cuda) or not (k.device == q.device and v.device == q.device):
+        raise RuntimeError("q, k, v must be device tensors on one device")
     if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
         raise ValueError("q, k, v must be contiguous")
     B, H, S, D = q.shape
@@ -197,6 +197,10 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = Fa
         raise ValueError("out must be a contiguous tensor of q's shape and dtype")
     if lse.shape != (B, H, S) or lse.dtype != torch.float32 or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 tensor of shape [B,H,S]")
+    # the kernels write through these pointers: a host (or other-device) buffer
+    # would hand the GPU an address it must not touch
+    if out.device != q.device or lse.device != q.device:
+        raise ValueError(f"out and lse must be on q's device {q.device}; got {out.device}, {lse.device}")
     stream = torch.cuda.current_stream(q.device).cuda_stream
     wl, wr = _window(window)
     status = fa_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
@@ -218,8 +222,8 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
         raise ValueError("q, o, dout must share one [B,H,S_q,D] shape and k, v one [B,H_kv,S_k,D] shape")
     if any(t.dtype != q.dtype for t in ts) or q.dtype not in (torch.float16, torch.bfloat16):
         raise ValueError("q, k, v, o, dout must share dtype float16 or bfloat16")
-    if not all(t.is_cuda for t in ts + (lse,)):
-        raise RuntimeError("all tensors must be device tensors")
+    if not all(t.is_cuda and t.device == q.device for t in ts + (lse,)):
+        raise RuntimeError("all tensors must be device tensors on one device")
     if not all(t.is_contiguous() for t in ts + (lse,)):
         raise ValueError("all tensors must be contiguous")
     B, H, S, D = q.shape

@@ -18,6 +18,9 @@ SOURCES = [os.path.join(HERE, "csrc", "fa_fwd.hip")]
 HEADERS = [os.path.join(HERE, "csrc", f) for f in ("fa_common.hpp", "fa_mfma.hpp", "fa_split.hpp", "fa_ksplit.hpp", "fa_f32.hpp", "fa_bwd.hpp", "fa_window.hpp", "fa_split_window.hpp")] + [
     os.path.join(ROOT, "include", "fa.h")]
 LIBRARY = os.path.join(HERE, "libfa.so")
+# the instruction-rate microbenchmarks (a measurement tool, separate library)
+MICRO_SOURCE = os.path.join(HERE, "csrc", "fa_micro.hip")
+MICRO_LIBRARY = os.path.join(HERE, "libfa_micro.so")
 
 ARCH = "gfx950"
 FLAGS = [
@@ -43,16 +46,22 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm toolchain required to build the HIP library)")
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source into LIBRARY; always recompiles."""
-    tmp = LIBRARY + ".tmp"
-    cmd = [hipcc(), *FLAGS, "-o", tmp, *SOURCES]
+def _compile(sources, output: str, verbose: bool) -> None:
+    tmp = output + ".tmp"
+    cmd = [hipcc(), *FLAGS, "-o", tmp, *sources]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{res.stderr[-8000:]}")
-    os.replace(tmp, LIBRARY)
+    os.replace(tmp, output)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source: LIBRARY (the attention kernels and their C ABI)
+    and MICRO_LIBRARY (the microbenchmarks); always recompiles."""
+    _compile(SOURCES, LIBRARY, verbose)
+    _compile([MICRO_SOURCE], MICRO_LIBRARY, verbose)
     return LIBRARY
 
 

@@ -253,7 +253,9 @@ void fa_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict
         row_frags<KS>(O + head, qrow[a], D, h, of[a]);
     }
     issue_order();
-    if (KSQ == 1 || tgb < tge) stage(P0{}, tgb);
+    // a block with no key tile (a window that leaves its rows no key, S_k < S_q)
+    // stages nothing: no LDS transfer may outlive the workgroup
+    if (tgb < tge) stage(P0{}, tgb);
     float delta[QB], lse2[QB];
 #pragma unroll
     for (int a = 0; a < QB; ++a) {

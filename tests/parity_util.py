@@ -91,6 +91,15 @@ def check_lse(l_gpu: np.ndarray, l_ref: np.ndarray, what: str = "lse") -> float:
     return rel
 
 
+def lse_errors(l_gpu: np.ndarray, l_ref: np.ndarray):
+    """(normwise, elementwise) lse errors: max|d| / max|ref| and max |d| / max(|ref|, 1)."""
+    if l_gpu.size == 0:
+        return 0.0, 0.0
+    d = np.abs(l_gpu - l_ref)
+    return (float(np.max(d)) / max(float(np.max(np.abs(l_ref))), 1e-30),
+            float(np.max(d / np.maximum(np.abs(l_ref), 1.0))))
+
+
 def sample_rows(B: int, H: int, S: int, n_random: int, seed: int) -> np.ndarray:
     """Flat row indices (b*H + h)*S + i: the first and last rows of every head, rows
     on both sides of every 32/64/128/256-row boundary of a few heads, and random rows."""

@@ -256,3 +256,32 @@ def test_ex_no_query_rows_is_a_no_op_forward(fa):
     assert xbcall(fa, q=0, k=0, v=0, o=0, dout=0, lse=0, dq=0, dk=0, dv=0, delta=0, Sq=0, Sk=0) == fa.FA_OK
     # the backward still owes dK = dV = 0 for the keys
     assert xbcall(fa, q=0, o=0, dout=0, lse=0, dq=0, delta=0, dk=0, Sq=0, Sk=512) == fa.FA_ERR_NULL_POINTER
+
+
+# ---- the microbenchmark library (include/fa_micro.h) --------------------------
+
+MICRO_HEADER = os.path.join(ROOT, "include", "fa_micro.h")
+
+
+def test_micro_exports_and_rejects_bad_arguments():
+    """libfa_micro.so exports every function fa_micro.h declares, its constants
+    match the binding's, and out-of-range arguments fail before any HIP call."""
+    from exact_tiled_attention_06_amd import micro
+    with open(MICRO_HEADER, encoding="utf-8") as f:
+        text = f.read()
+    lib = micro.library()
+    for name in set(re.findall(r"\b(fa_micro\w*)\s*\(", re.sub(r"/\*.*?\*/", "", text, flags=re.S))):
+        assert hasattr(lib, name), f"{name} declared in include/fa_micro.h but not exported"
+    defs = {m.group(1): int(m.group(2)) for m in re.finditer(r"#define\s+(FA_MICRO_\w+)\s+(-?\d+)", text)}
+    assert defs["FA_MICRO_OP_EXP"] == micro.OP_EXP and defs["FA_MICRO_OP_MAX3"] == micro.OP_MAX3
+    assert defs["FA_MICRO_MIXED"] == micro.MIXED and defs["FA_MICRO_SPLIT"] == micro.SPLIT
+    err = defs["FA_MICRO_ERR_ARG"]
+    out = 1 << 20  # never dereferenced: every call below fails validation first
+    assert lib.fa_micro(99, 4, 0, micro.MIXED, 4, 10, out, None) == err      # op
+    assert lib.fa_micro(micro.OP_EXP, 3, 0, micro.MIXED, 4, 10, out, None) == err   # k
+    assert lib.fa_micro(micro.OP_EXP, 4, 2, micro.MIXED, 4, 10, out, None) == err   # agpr
+    assert lib.fa_micro(micro.OP_EXP, 4, 0, 7, 4, 10, out, None) == err             # mode
+    assert lib.fa_micro(micro.OP_EXP, 4, 0, micro.SPLIT, 4, 10, out, None) == err   # split needs 8 waves
+    assert lib.fa_micro(micro.OP_EXP, 4, 0, micro.MIXED, 9, 10, out, None) == err   # waves
+    assert lib.fa_micro(micro.OP_EXP, 4, 0, micro.MIXED, 4, 0, out, None) == err    # iters
+    assert lib.fa_micro(micro.OP_EXP, 4, 0, micro.MIXED, 4, 10, None, None) == err  # cycles

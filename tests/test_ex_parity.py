@@ -67,7 +67,7 @@ def test_fwd_window_and_groups_elementwise(dtype, D, causal):
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-@pytest.mark.parametrize("D", [32, 64, 128])
+@pytest.mark.parametrize("D", [16, 32, 64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_bwd_window_and_groups_elementwise(dtype, D, causal):
     """O and lse from the oracle (as stored), gradients against the oracle's."""

@@ -99,7 +99,7 @@ def test_fwd_rect_window_empty_rows(dtype, D, causal):
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-@pytest.mark.parametrize("D", [32, 64, 128])
+@pytest.mark.parametrize("D", [16, 32, 64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_bwd_rect_elementwise(dtype, D, causal):
     """O and lse from the oracle (as stored; -inf for rows without keys),
@@ -143,7 +143,7 @@ def test_rect_large_grid_sampled(D, dtype):
         o_ref, l_ref = oracle.attention_rows(to_f64(q), to_f64(k), to_f64(v), causal, scale, rows)
         check_o(to_f64(o).reshape(-1, D)[rows], o_ref, dtype, f"O {what}")
         check_lse(to_f64(lse).reshape(-1)[rows], l_ref, f"lse {what}")
-        if dtype == "f32" or D == 16:
+        if dtype == "f32":
             continue
         dq, dk, dv = fa.backward(qd, kd, vd, o, lse, dd, causal=causal, scale=scale)
         torch.cuda.synchronize()

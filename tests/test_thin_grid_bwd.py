@@ -53,7 +53,7 @@ CASES = [
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-@pytest.mark.parametrize("D", [32, 64, 128])
+@pytest.mark.parametrize("D", [16, 32, 64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_thin_grid_bwd_elementwise(dtype, D, causal):
     scale = fp32(1 / math.sqrt(D))
