@@ -21,6 +21,9 @@ import this package before the library exists.
     fa_fwd_ex / fa_bwd_ex(...)
         the C entry points with grouped K/V heads (H_kv), separate query and
         key lengths (S_q, S_k) and a sliding window;
+    fa_bwd_noalloc(...)
+        fa_bwd_ex without the delta workspace argument (the library's static
+        device array), for callers that cannot allocate;
     backward(q, k, v, o, lse, dout, causal=False, scale=None, window=None) -> (dq, dk, dv)
         gradients for the upstream gradient dout, from the forward's o and lse;
         allocates the outputs and the D workspace and calls fa_bwd.
@@ -48,6 +51,7 @@ FA_ERR_TOO_LARGE = 8
 FA_ERR_LAUNCH = 9
 FA_ERR_ALIGNMENT = 10
 FA_ERR_WINDOW = 11
+FA_ERR_WORKSPACE = 12
 
 FA_DTYPE_F32 = 0
 FA_DTYPE_F16 = 1
@@ -57,7 +61,8 @@ DTYPE_CODES = {torch.float32: FA_DTYPE_F32, torch.float16: FA_DTYPE_F16, torch.b
 
 # argument problems map to ValueError, runtime problems to RuntimeError
 _VALUE_ERRORS = {FA_ERR_NULL_POINTER, FA_ERR_SHAPE, FA_ERR_HEAD_DIM, FA_ERR_DTYPE, FA_ERR_CAUSAL,
-                 FA_ERR_SCALE, FA_ERR_ALIAS, FA_ERR_TOO_LARGE, FA_ERR_ALIGNMENT, FA_ERR_WINDOW}
+                 FA_ERR_SCALE, FA_ERR_ALIAS, FA_ERR_TOO_LARGE, FA_ERR_ALIGNMENT, FA_ERR_WINDOW,
+                 FA_ERR_WORKSPACE}
 
 
 def _load() -> ctypes.CDLL:
@@ -77,6 +82,8 @@ def _load() -> ctypes.CDLL:
     lib.fa_fwd_ex.argtypes = [P] * 5 + [I64] * 6 + [I, I64, I64, F, I, P]
     lib.fa_bwd_ex.restype = I
     lib.fa_bwd_ex.argtypes = [P] * 10 + [I64] * 6 + [I, I64, I64, F, I, P]
+    lib.fa_bwd_noalloc.restype = I
+    lib.fa_bwd_noalloc.argtypes = [P] * 9 + [I64] * 6 + [I, I64, I64, F, I, P]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_status_string.argtypes = [ctypes.c_int]
     return lib
@@ -140,6 +147,15 @@ def fa_bwd_ex(q: int, k: int, v: int, o: int, dout: int, lse: int, dq: int, dk: 
     return int(library().fa_bwd_ex(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, H_kv, S_q, S_k, D,
                                    int(causal), int(window_left), int(window_right), float(scale), int(dtype),
                                    stream))
+
+
+def fa_bwd_noalloc(q: int, k: int, v: int, o: int, dout: int, lse: int, dq: int, dk: int, dv: int,
+                   B: int, H: int, H_kv: int, S_q: int, S_k: int, D: int, causal: int, window_left: int,
+                   window_right: int, scale: float, dtype: int, stream: int) -> int:
+    """fa_bwd_ex without the delta workspace (the library's static array, for
+    callers that cannot allocate); returns the status code."""
+    return int(library().fa_bwd_noalloc(q, k, v, o, dout, lse, dq, dk, dv, B, H, H_kv, S_q, S_k, D, int(causal),
+                                        int(window_left), int(window_right), float(scale), int(dtype), stream))
 
 
 def _window(window):

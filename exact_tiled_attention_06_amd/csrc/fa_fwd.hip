@@ -9,6 +9,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include <hip/hip_runtime.h>
 
 #include "../../include/fa.h"
@@ -311,34 +313,82 @@ int clip_window(int64_t w, int64_t S) { return (w < 0 || w >= S) ? -1 : (int)w; 
 
 }  // namespace
 
-extern "C" int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const void* dout,
-                         const float* lse, void* dq, void* dk, void* dv, float* delta, int64_t B, int64_t H,
-                         int64_t H_kv, int64_t S_q, int64_t S_k, int64_t D, int causal, int64_t window_left,
-                         int64_t window_right, float scale, int dtype, void* stream) {
+// ------------------------------------------------ backward: the entry points
+
+namespace {
+
+// The D = rowsum(dO o O) workspace of fa_bwd_noalloc: a static device array, one
+// copy per GPU, held until the process ends.  Host code never passes the
+// array's name to a kernel (on the host it only stands in for the symbol): each
+// device's address comes from hipGetSymbolAddress, taken once per device with
+// that device current, and only that address is used.
+constexpr int64_t kScratchFloats = (int64_t)1 << 22;  // 16 MiB: B * H * S_q <= 4,194,304
+__device__ __align__(256) float scratch[kScratchFloats];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mutex;
+float* scratch_ptr[kMaxDevices] = {};
+
+// The workspace address on the device that runs `stream` (NULL: the current
+// device), looked up on the first call for that device.
+int scratch_for(hipStream_t stream, float** out) {
+    int cur = -1, dev = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return FA_ERR_LAUNCH;
+    if (stream) {
+        hipDevice_t d;
+        if (hipStreamGetDevice(stream, &d) != hipSuccess) return FA_ERR_LAUNCH;
+        dev = (int)d;
+    } else {
+        dev = cur;
+    }
+    if (dev < 0 || dev >= kMaxDevices) return FA_ERR_LAUNCH;
+    std::lock_guard<std::mutex> lock(scratch_mutex);
+    if (!scratch_ptr[dev]) {
+        if (dev != cur && hipSetDevice(dev) != hipSuccess) return FA_ERR_LAUNCH;
+        void* p = nullptr;
+        const hipError_t rc = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (dev != cur && hipSetDevice(cur) != hipSuccess) return FA_ERR_LAUNCH;
+        if (rc != hipSuccess || !p) return FA_ERR_LAUNCH;
+        scratch_ptr[dev] = (float*)p;
+    }
+    *out = scratch_ptr[dev];
+    return FA_OK;
+}
+
+// fa_bwd_ex's work; with `static_delta` the D workspace is the library's own
+// static array (`delta` is ignored) instead of the caller's buffer.
+int bwd_entry(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+              void* dq, void* dk, void* dv, float* delta, bool static_delta, int64_t B, int64_t H, int64_t H_kv,
+              int64_t S_q, int64_t S_k, int64_t D, int causal, int64_t window_left, int64_t window_right,
+              float scale, int dtype, void* stream) {
     // ---- argument checks: no HIP call before all of them pass ----------------
     int rc = check_problem(B, H, H_kv, S_q, S_k, D, causal, window_left, window_right, scale);
     if (rc == FA_ERR_SHAPE || rc == FA_ERR_HEAD_DIM) return rc;
     if (dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
     if (rc != FA_OK) return rc;
     if (B == 0 || H == 0 || (S_q == 0 && S_k == 0)) return FA_OK;
-    if (S_q > 0 && (!q || !o || !dout || !lse || !dq || !delta)) return FA_ERR_NULL_POINTER;
+    if (S_q > 0 && (!q || !o || !dout || !lse || !dq || (!static_delta && !delta))) return FA_ERR_NULL_POINTER;
     if (S_k > 0 && (!k || !v || !dk || !dv)) return FA_ERR_NULL_POINTER;
     const int64_t S = S_q > S_k ? S_q : S_k;
     if ((rc = check_sizes(B, H, S, D)) != FA_OK) return rc;
     if (S * D * 2 > 2147483647) return FA_ERR_TOO_LARGE;
     const int64_t BH = B * H;
+    if (static_delta && BH * S_q > kScratchFloats) return FA_ERR_WORKSPACE;
     const int64_t tb = BH * S_q * D * 2, kvb = B * H_kv * S_k * D * 2, vb = BH * S_q * 4;
     if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)dout | (uintptr_t)dq |
          (uintptr_t)dk | (uintptr_t)dv) & 15)
         return FA_ERR_ALIGNMENT;
-    if (((uintptr_t)lse | (uintptr_t)delta) & 3) return FA_ERR_ALIGNMENT;
-    // every output (dq, dk, dv, delta) apart from every other buffer
+    if (((uintptr_t)lse | (static_delta ? 0 : (uintptr_t)delta)) & 3) return FA_ERR_ALIGNMENT;
+    // every output (dq, dk, dv, delta) apart from every other buffer (the
+    // static workspace is an allocation of its own)
+    const int nout = static_delta ? 3 : 4;
     const void* outs[4] = {dq, dk, dv, delta};
     const int64_t out_bytes[4] = {tb, kvb, kvb, vb};
     const void* all[10] = {q, k, v, o, dout, lse, dq, dk, dv, delta};
     const int64_t all_bytes[10] = {tb, kvb, kvb, tb, tb, vb, tb, kvb, kvb, vb};
-    for (int i = 0; i < 4; ++i)
-        for (int j = 0; j < 10; ++j)
+    const int nall = static_delta ? 9 : 10;
+    for (int i = 0; i < nout; ++i)
+        for (int j = 0; j < nall; ++j)
             if (j != 6 + i && overlaps(outs[i], out_bytes[i], all[j], all_bytes[j])) return FA_ERR_ALIAS;
 
     // no keys: every dQ is 0 (dK, dV are empty); no queries: dK = dV = 0
@@ -347,10 +397,31 @@ extern "C" int fa_bwd_ex(const void* q, const void* k, const void* v, const void
         if ((rc = fill_words(dk, 0u, kvb, (hipStream_t)stream)) != FA_OK) return rc;
         return fill_words(dv, 0u, kvb, (hipStream_t)stream);
     }
+    // the dQ kernel writes D for every query row before the dK/dV kernel reads
+    // it, so the workspace needs no clearing
+    if (static_delta && (rc = scratch_for((hipStream_t)stream, &delta)) != FA_OK) return rc;
     Bwd a{q, k, v, o, dout, lse, dq, dk, dv, delta, (int)S_q, (int)S_k, (int)BH, (int)(H / H_kv),
           clip_window(window_left, S), clip_window(window_right, S),
           (float)((double)scale * 1.4426950408889634), scale, (hipStream_t)stream};
     return causal ? dispatch_bwd<true>(D, dtype, a) : dispatch_bwd<false>(D, dtype, a);
+}
+
+}  // namespace
+
+extern "C" int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                         const float* lse, void* dq, void* dk, void* dv, float* delta, int64_t B, int64_t H,
+                         int64_t H_kv, int64_t S_q, int64_t S_k, int64_t D, int causal, int64_t window_left,
+                         int64_t window_right, float scale, int dtype, void* stream) {
+    return bwd_entry(q, k, v, o, dout, lse, dq, dk, dv, delta, false, B, H, H_kv, S_q, S_k, D, causal, window_left,
+                     window_right, scale, dtype, stream);
+}
+
+extern "C" int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                              const float* lse, void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t H_kv,
+                              int64_t S_q, int64_t S_k, int64_t D, int causal, int64_t window_left,
+                              int64_t window_right, float scale, int dtype, void* stream) {
+    return bwd_entry(q, k, v, o, dout, lse, dq, dk, dv, nullptr, true, B, H, H_kv, S_q, S_k, D, causal,
+                     window_left, window_right, scale, dtype, stream);
 }
 
 extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
@@ -417,6 +488,7 @@ extern "C" const char* fa_status_string(int status) {
         case FA_ERR_LAUNCH: return "the HIP runtime rejected the kernel launch";
         case FA_ERR_ALIGNMENT: return "[B,H,S,D] tensors must be 16-byte aligned, lse and delta 4-byte aligned";
         case FA_ERR_WINDOW: return "window bounds must be >= -1 (-1: no limit on that side)";
+        case FA_ERR_WORKSPACE: return "B * H * S_q exceeds the static workspace of fa_bwd_noalloc (4,194,304 rows)";
         default: return "unknown status";
     }
 }

@@ -53,6 +53,7 @@ extern "C" {
 #define FA_ERR_LAUNCH 9         /* the HIP runtime rejected the kernel launch */
 #define FA_ERR_ALIGNMENT 10     /* a [B,H,S,D] tensor not 16-byte aligned, or lse / delta not 4-byte aligned */
 #define FA_ERR_WINDOW 11        /* a window bound is below -1 */
+#define FA_ERR_WORKSPACE 12     /* fa_bwd_noalloc: B * H * S_q exceeds its static workspace */
 
 /* ---- element types (the dtype argument) --------------------------------- */
 #define FA_DTYPE_F32 0
@@ -182,6 +183,32 @@ int fa_bwd_ex(const void *q, const void *k, const void *v, const void *o, const 
               int64_t B, int64_t H, int64_t H_kv, int64_t S_q, int64_t S_k, int64_t D,
               int causal, int64_t window_left, int64_t window_right,
               float scale, int dtype, void *stream);
+
+/*
+ * fa_bwd_noalloc -- fa_bwd_ex without the delta workspace argument, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): the D = rowsum(dO o O)
+ * workspace is a static device array inside the library, one per GPU, of
+ * 4,194,304 floats (16 MiB, held until the process ends).
+ *
+ *   every argument as for fa_bwd_ex (same kernels, same results); there is
+ *   no delta.
+ *
+ * Limit: B * H * S_q <= 4,194,304 (FA_ERR_WORKSPACE otherwise, before any HIP
+ * call).  The call allocates and frees nothing; on its first use on a device
+ * it looks up that device's copy of the array (hipGetSymbolAddress, with the
+ * device that runs `stream` current).  The array keeps the last call's D
+ * values; nothing in it needs to start at zero.
+ *
+ * Calls on one GPU share its array: two calls whose executions overlap on the
+ * same GPU (e.g. on two streams without ordering between them) race on it and
+ * must not be issued.  Calls on one stream are ordered and safe.
+ */
+int fa_bwd_noalloc(const void *q, const void *k, const void *v, const void *o, const void *dout,
+                   const float *lse, void *dq, void *dk, void *dv,
+                   int64_t B, int64_t H, int64_t H_kv, int64_t S_q, int64_t S_k, int64_t D,
+                   int causal, int64_t window_left, int64_t window_right,
+                   float scale, int dtype, void *stream);
 
 /* A static, human-readable description of a status code (never NULL). */
 const char *fa_status_string(int status);

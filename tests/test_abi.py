@@ -285,3 +285,15 @@ def test_micro_exports_and_rejects_bad_arguments():
     assert lib.fa_micro(micro.OP_EXP, 4, 0, micro.MIXED, 9, 10, out, None) == err   # waves
     assert lib.fa_micro(micro.OP_EXP, 4, 0, micro.MIXED, 4, 0, out, None) == err    # iters
     assert lib.fa_micro(micro.OP_EXP, 4, 0, micro.MIXED, 4, 10, None, None) == err  # cycles
+
+
+def test_bwd_noalloc_rejects_oversized_problem(fa):
+    """fa_bwd_noalloc refuses B * H * S_q beyond its static workspace (4,194,304
+    rows) with FA_ERR_WORKSPACE, before any HIP call."""
+    st = fa.fa_bwd_noalloc(P, 2 * P, 3 * P, 4 * P, 5 * P, 6 * P, 7 * P, 8 * P, 9 * P, 1, 1, 1, 4194305, 64, 64,
+                           0, -1, -1, 0.125, fa.FA_DTYPE_F16, 0)
+    assert st == fa.FA_ERR_WORKSPACE
+    # the argument checks of fa_bwd_ex come first: a bad head dim wins
+    st = fa.fa_bwd_noalloc(P, 2 * P, 3 * P, 4 * P, 5 * P, 6 * P, 7 * P, 8 * P, 9 * P, 1, 1, 1, 4194305, 64, 48,
+                           0, -1, -1, 0.125, fa.FA_DTYPE_F16, 0)
+    assert st == fa.FA_ERR_HEAD_DIM
