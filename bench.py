@@ -25,6 +25,19 @@ Prints one JSON line.  Also reported:
                 kernel time, and the oracle's gradients over one head as its
                 CPU baseline (--no-backward skips it).
 
+  roofline.exp_valu  the vector-side roof: v_exp / v_fma / v_add / v_cvt_pk
+                issue rates measured in the same run (libfa_micro.so), turned
+                into SIMD-cycles per attended (query, key) pair against the
+                MFMA cycles per pair, with the TFLOP/s each side allows alone
+                and with no overlap;
+  configs       one record per configuration workload and mask (single-head
+                fp32, the headless batch both ways, the multi-head causal
+                workload, the long bf16 sequence, the 20 sweep points): kernel
+                microseconds from a replayed HIP graph, TFLOP/s, fraction of
+                peak, algorithmic HBM GB/s, and the errors of O and lse against
+                the float64 oracle over every element (--no-configs,
+                --no-parity skip them).
+
 Options: --gpus N (only 1 is supported: the kernel runs on one GPU),
 --steps K (timed launches), --warmup W, --workload NAME, --no-cpu-baseline,
 --sweep FILE (also time every named workload and write one JSON line per
@@ -214,6 +227,80 @@ def cpu_baseline(w, causal):
     }
 
 
+
+# The five configurations of the benchmark plan: single-head fp32, the headless
+# batch (both masks), the multi-head causal workload, the long bf16 sequence and
+# the 20-point causal fp16 sweep.
+CONFIG_WORKLOADS = (["single_head_f32", "batch_f16", "multihead_causal", "long_seq_bf16"]
+                    + [f"sweep_D{d}_S{s}" for d in (16, 32, 64, 128) for s in (256, 1024, 4096, 8192, 16384)])
+
+
+def config_records(fa, torch, parity=True):
+    """One record per configuration workload and mask: kernel microseconds timed
+    from a replayed HIP graph, TFLOP/s, fraction of the dense peak of its dtype,
+    algorithmic HBM GB/s and, with parity, the errors of O and lse against the
+    float64 oracle over every element (max |dO| absolute for fp16/bf16, normwise
+    relative for fp32; lse normwise and elementwise relative)."""
+    import numpy as np
+    import workloads
+    recs = []
+    for name in CONFIG_WORKLOADS:
+        w = workloads.BY_NAME[name]
+        for c in w.causal:
+            us = time_graph(fa, torch, w, c) * 1e3
+            tf = w.flops(c) / (us * 1e-6) / 1e12
+            rec = {"workload": name, "causal": c, "dtype": w.dtype, "B": w.B, "H": w.H, "S": w.S, "D": w.D,
+                   "kernel_us": round(us, 2), "tflops": round(tf, 1),
+                   "frac": round(tf / PEAK_MFMA_TFLOPS[w.dtype], 4),
+                   "hbm_gbs_algorithmic": round(w.hbm_bytes() / (us * 1e-6) / 1e9, 1)}
+            if parity:
+                import oracle
+                q, k, v = workloads.workload_inputs(w)
+                o, lse = fa.forward(q.to("cuda:0"), k.to("cuda:0"), v.to("cuda:0"), causal=c, scale=w.scale)
+                torch.cuda.synchronize()
+                o_ref, l_ref = oracle.attention(q.double().numpy(), k.double().numpy(), v.double().numpy(), c,
+                                                w.scale)
+                d_o = np.abs(o.cpu().double().numpy() - o_ref)
+                d_l = np.abs(lse.cpu().double().numpy() - l_ref)
+                rec["max_abs_dO"] = float(d_o.max()) if w.dtype != "f32" else None
+                rec["o_rel_normwise"] = float(d_o.max() / np.abs(o_ref).max())
+                rec["lse_rel_normwise"] = float(d_l.max() / np.abs(l_ref).max())
+                rec["lse_rel_elementwise"] = float((d_l / np.maximum(np.abs(l_ref), 1.0)).max())
+            recs.append(rec)
+            print(f"config {name} causal={c}: {us:.1f} us, {tf:.1f} TFLOP/s ({100 * rec['frac']:.1f} % of peak)"
+                  + (f", max|dO| {rec.get('max_abs_dO')}, lse rel {rec['lse_rel_normwise']:.2e}" if parity else ""),
+                  file=sys.stderr, flush=True)
+    return recs
+
+
+def exp_valu_roof(D):
+    """The vector-side roof of the attention loop, from instruction rates measured
+    now (libfa_micro.so, two waves per SIMD): per attended (query, key) pair the
+    forward issues one v_exp_f32, one v_fma_f32 (S*c - m), one v_add_f32 (row
+    sum) and half a v_cvt_pk (P to 16 bits) per lane, against 4*D FLOPs of
+    32x32x16 MFMA.  Returns SIMD-cycles per pair on each side and the TFLOP/s
+    each side alone would allow at the peak's 2.4 GHz on 1024 SIMDs, plus the
+    bound with no overlap of the two."""
+    from exact_tiled_attention_06_amd import micro
+    it = 400
+    micro.run(micro.OP_EXP, 4, False, micro.VECTOR, 8, 10)  # warm-up
+    per = {}
+    for op, name in ((micro.OP_EXP, "exp"), (micro.OP_FMA, "fma"), (micro.OP_ADD, "add"), (micro.OP_CVT, "cvt")):
+        c = micro.run(op, 4, False, micro.VECTOR, 8, it)
+        per[name] = max(c) / (it * 32) / 2  # SIMD-cycles per wave64 instruction (two waves share a SIMD)
+    c = micro.run(micro.OP_EXP, 0, False, micro.PRODUCTS, 8, it)
+    mfma = max(c) / (it * 8) / 2
+    vec_pair = (per["exp"] + per["fma"] + per["add"] + 0.5 * per["cvt"]) / 64
+    mfma_pair = 4 * D / (2 * 32 * 32 * 16) * mfma
+    scale = 1024 * 2.4e9 * 4 * D / 1e12
+    return {"vector_cycles_per_pair": round(vec_pair, 4), "mfma_cycles_per_pair": round(mfma_pair, 4),
+            "issue_cycles": {k: round(v, 2) for k, v in per.items()} | {"mfma_32x32x16": round(mfma, 2)},
+            "vector_roof_tflops": round(scale / vec_pair, 1), "mfma_roof_tflops": round(scale / mfma_pair, 1),
+            "no_overlap_tflops": round(scale / (vec_pair + mfma_pair), 1),
+            "note": "SIMD-cycles per attended pair at two waves per SIMD (measured issue rates); the loop "
+                    "cannot run faster than either roof, and runs at the no-overlap bound if vector work and "
+                    "MFMAs never overlap"}
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -227,6 +314,10 @@ def main():
     ap.add_argument("--traffic-bytes", type=float, default=None,
                     help="HBM bytes per launch measured with rocprofv3 counters")
     ap.add_argument("--sweep", default=None, help="write per-workload JSON lines to this file")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-configuration records (graph-timed, with oracle errors)")
+    ap.add_argument("--no-parity", action="store_true",
+                    help="per-configuration records without the oracle comparison")
     ap.add_argument("--micro", default=None,
                     help="instead of attention, run the instruction-rate microbenchmarks (libfa_micro.so) and "
                          "write their table, one JSON line per probe, to this file")
@@ -365,6 +456,11 @@ def main():
                     f.write(json.dumps(rec) + "\n")
                     print(f"sweep {sw.name} causal={c}: {rec['tflops']:.1f} TFLOP/s "
                           f"({avg * 1e3:.1f} us)", file=sys.stderr, flush=True)
+
+    if w.dtype in ("f16", "bf16"):
+        out["roofline"]["exp_valu"] = exp_valu_roof(w.D)
+    if not args.no_configs:
+        out["configs"] = config_records(fa, torch, parity=not args.no_parity)
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, causal)

@@ -84,6 +84,10 @@ __device__ __forceinline__ float halves_sum(float x) {
     return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
 }
 
+// Instruction classes of __builtin_amdgcn_sched_group_barrier masks.
+constexpr int kSchedValu = 0x2;
+constexpr int kSchedMfma = 0x8;
+
 // Make a loaded value opaque to the optimiser, so that it stays in registers
 // rather than being re-loaded from memory later when registers are scarce.
 __device__ __forceinline__ void pin(u32x4& v) {
