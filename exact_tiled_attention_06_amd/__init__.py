@@ -21,6 +21,8 @@ import this package before the library exists.
     fa_fwd_ex / fa_bwd_ex(...)
         the C entry points with grouped K/V heads (H_kv), separate query and
         key lengths (S_q, S_k) and a sliding window;
+    fa_fwd_single_buffered(...)
+        race check: fa_fwd's two-block kernel with single-buffered K/V staging;
     fa_bwd_noalloc(...)
         fa_bwd_ex without the delta workspace argument (the library's static
         device array), for callers that cannot allocate;
@@ -52,6 +54,7 @@ FA_ERR_LAUNCH = 9
 FA_ERR_ALIGNMENT = 10
 FA_ERR_WINDOW = 11
 FA_ERR_WORKSPACE = 12
+FA_ERR_UNSUPPORTED = 13
 
 FA_DTYPE_F32 = 0
 FA_DTYPE_F16 = 1
@@ -62,7 +65,7 @@ DTYPE_CODES = {torch.float32: FA_DTYPE_F32, torch.float16: FA_DTYPE_F16, torch.b
 # argument problems map to ValueError, runtime problems to RuntimeError
 _VALUE_ERRORS = {FA_ERR_NULL_POINTER, FA_ERR_SHAPE, FA_ERR_HEAD_DIM, FA_ERR_DTYPE, FA_ERR_CAUSAL,
                  FA_ERR_SCALE, FA_ERR_ALIAS, FA_ERR_TOO_LARGE, FA_ERR_ALIGNMENT, FA_ERR_WINDOW,
-                 FA_ERR_WORKSPACE}
+                 FA_ERR_WORKSPACE, FA_ERR_UNSUPPORTED}
 
 
 def _load() -> ctypes.CDLL:
@@ -82,6 +85,8 @@ def _load() -> ctypes.CDLL:
     lib.fa_fwd_ex.argtypes = [P] * 5 + [I64] * 6 + [I, I64, I64, F, I, P]
     lib.fa_bwd_ex.restype = I
     lib.fa_bwd_ex.argtypes = [P] * 10 + [I64] * 6 + [I, I64, I64, F, I, P]
+    lib.fa_fwd_single_buffered.restype = I
+    lib.fa_fwd_single_buffered.argtypes = [P] * 5 + [I64] * 4 + [I, F, I, P]
     lib.fa_bwd_noalloc.restype = I
     lib.fa_bwd_noalloc.argtypes = [P] * 9 + [I64] * 6 + [I, I64, I64, F, I, P]
     lib.fa_status_string.restype = ctypes.c_char_p
@@ -147,6 +152,14 @@ def fa_bwd_ex(q: int, k: int, v: int, o: int, dout: int, lse: int, dq: int, dk: 
     return int(library().fa_bwd_ex(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, H_kv, S_q, S_k, D,
                                    int(causal), int(window_left), int(window_right), float(scale), int(dtype),
                                    stream))
+
+
+def fa_fwd_single_buffered(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, S: int, D: int,
+                           causal: int, scale: float, dtype: int, stream: int) -> int:
+    """Race check: fa_fwd on the two-block kernel with single-buffered K/V
+    staging (bit-identical results expected); returns the status code."""
+    return int(library().fa_fwd_single_buffered(q, k, v, o, lse, B, H, S, D, int(causal), float(scale),
+                                                int(dtype), stream))
 
 
 def fa_bwd_noalloc(q: int, k: int, v: int, o: int, dout: int, lse: int, dq: int, dk: int, dv: int,

@@ -74,6 +74,7 @@ struct Fwd {
     int wl, wr;         // window (left, right); -1: no limit on that side
     float c;            // scale * log2(e)
     hipStream_t stream;
+    bool single;        // race check: the single-buffered two-block kernel
 };
 
 // Fills n 32-bit words with `value` (outputs of problems without keys or
@@ -93,14 +94,14 @@ int fill_words(void* p, uint32_t value, int64_t bytes, hipStream_t stream) {
     return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
-template <typename T, typename Cfg>
+template <typename T, typename Cfg, bool SINGLE = false>
 int launch_cfg(const Fwd& a) {
     const int n_qblk = (a.Sq + Cfg::BM - 1) / Cfg::BM;
     const int64_t grid = (int64_t)n_qblk * a.BH;
     if (grid > (int64_t)1 << 24) return FA_ERR_TOO_LARGE;
     (void)hipGetLastError();  // clear a stale error so the check below sees this launch only
     if constexpr (Cfg::QB == 2 && Cfg::KB == 1 && Cfg::PIPE)
-        hipLaunchKernelGGL((fa_fwd_split_kernel<T, Cfg>), dim3((unsigned)grid), dim3(Cfg::NT), 0, a.stream,
+        hipLaunchKernelGGL((fa_fwd_split_kernel<T, Cfg, SINGLE>), dim3((unsigned)grid), dim3(Cfg::NT), 0, a.stream,
                            (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o,
                            a.lse, a.Sq, a.Sk, a.BH, n_qblk, a.G, a.c);
     else
@@ -147,11 +148,19 @@ int launch_window(const Fwd& a) {
 
 template <typename T, int D, bool CAUSAL>
 int launch_mfma(const Fwd& a) {
+    if (a.single && (a.wl >= 0 || a.wr >= 0)) return FA_ERR_UNSUPPORTED;
     if (a.wl >= 0 || a.wr >= 0) return launch_window<T, D, CAUSAL>(a);
     using TL = Tiles<D>;
     using Large = MfmaConfig<D, CAUSAL, TL::QB, TL::NW, TL::BN, TL::PIPE, 2, TL::TBN>;
     using Small = MfmaConfig<D, CAUSAL, TL::SMALL_QB, TL::SMALL_NW, TL::SMALL_BN, TL::SMALL_PIPE>;
     const int64_t large_grid = (int64_t)((a.Sq + Large::BM - 1) / Large::BM) * a.BH;
+    if (a.single) {
+        // the race check exists for the double-buffered two-block kernel only
+        if constexpr (D == 32 || D == 64) {
+            if (large_grid >= kFullGrid) return launch_cfg<T, Large, true>(a);
+        }
+        return FA_ERR_UNSUPPORTED;
+    }
     if (large_grid >= kFullGrid) return launch_cfg<T, Large>(a);
     // Thinner grids split each query block's keys over the 4 waves of its
     // workgroup.  Measured on the B=8 H=1 sweep: at D <= 64 blocks of 64 rows
@@ -185,7 +194,7 @@ int dispatch_dtype(int dtype, const Fwd& a) {
     switch (dtype) {
         case FA_DTYPE_F16: return launch_mfma<F16, D, CAUSAL>(a);
         case FA_DTYPE_BF16: return launch_mfma<BF16, D, CAUSAL>(a);
-        default: return launch_f32<D, CAUSAL>(a);
+        default: return a.single ? FA_ERR_UNSUPPORTED : launch_f32<D, CAUSAL>(a);
     }
 }
 
@@ -431,9 +440,12 @@ extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o
                      stream);
 }
 
-extern "C" int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
-                         int64_t H_kv, int64_t S_q, int64_t S_k, int64_t D, int causal, int64_t window_left,
-                         int64_t window_right, float scale, int dtype, void* stream) {
+namespace {
+
+// fa_fwd_ex's work; `single` selects the single-buffered race-check variant.
+int fwd_entry(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H, int64_t H_kv,
+              int64_t S_q, int64_t S_k, int64_t D, int causal, int64_t window_left, int64_t window_right,
+              float scale, int dtype, void* stream, bool single) {
     // ---- argument checks: no HIP call before all of them pass ----------------
     int rc = check_problem(B, H, H_kv, S_q, S_k, D, causal, window_left, window_right, scale);
     if (rc == FA_ERR_SHAPE || rc == FA_ERR_HEAD_DIM) return rc;
@@ -465,8 +477,23 @@ extern "C" int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, f
     }
     // c = scale * log2(e), rounded once to fp32: scores enter exp2 as S*c - m.
     Fwd a{q, k, v, o, lse, (int)S_q, (int)S_k, (int)BH, (int)(H / H_kv), clip_window(window_left, S),
-          clip_window(window_right, S), (float)((double)scale * 1.4426950408889634), (hipStream_t)stream};
+          clip_window(window_right, S), (float)((double)scale * 1.4426950408889634), (hipStream_t)stream, single};
     return causal ? dispatch_d<true>(D, dtype, a) : dispatch_d<false>(D, dtype, a);
+}
+
+}  // namespace
+
+extern "C" int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+                         int64_t H_kv, int64_t S_q, int64_t S_k, int64_t D, int causal, int64_t window_left,
+                         int64_t window_right, float scale, int dtype, void* stream) {
+    return fwd_entry(q, k, v, o, lse, B, H, H_kv, S_q, S_k, D, causal, window_left, window_right, scale, dtype,
+                     stream, false);
+}
+
+extern "C" int fa_fwd_single_buffered(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                                      int64_t H, int64_t S, int64_t D, int causal, float scale, int dtype,
+                                      void* stream) {
+    return fwd_entry(q, k, v, o, lse, B, H, H, S, S, D, causal, -1, -1, scale, dtype, stream, true);
 }
 
 extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
@@ -488,6 +515,7 @@ extern "C" const char* fa_status_string(int status) {
         case FA_ERR_LAUNCH: return "the HIP runtime rejected the kernel launch";
         case FA_ERR_ALIGNMENT: return "[B,H,S,D] tensors must be 16-byte aligned, lse and delta 4-byte aligned";
         case FA_ERR_WINDOW: return "window bounds must be >= -1 (-1: no limit on that side)";
+        case FA_ERR_UNSUPPORTED: return "fa_fwd_single_buffered: only the two-block kernel (D = 32, 64, fp16 / bf16, B*H*ceil(S/256) >= 512, no window) has a single-buffered variant";
         case FA_ERR_WORKSPACE: return "B * H * S_q exceeds the static workspace of fa_bwd_noalloc (4,194,304 rows)";
         default: return "unknown status";
     }

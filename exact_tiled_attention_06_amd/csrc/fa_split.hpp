@@ -164,7 +164,13 @@ struct SplitTile {
     }
 };
 
-template <typename T, typename Cfg>
+// SINGLE = true is the race check of the double-buffered staging: one K and one
+// V buffer, the next tile's transfers issued only after a barrier that follows
+// every wave's last fragment read of the current one.  The arithmetic and its
+// order are the same, so its O and lse must equal the double-buffered kernel's
+// bit for bit; a difference would expose a read of a buffer still being
+// refilled.
+template <typename T, typename Cfg, bool SINGLE = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(Cfg::NT, Cfg::NT), amdgpu_waves_per_eu(Cfg::OCC, Cfg::OCC)))
 void fa_fwd_split_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                          const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE, int Sq, int Sk,
@@ -187,8 +193,10 @@ void fa_fwd_split_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
     __shared__ __attribute__((aligned(1024))) char k_lds1[Cfg::TILE];
     __shared__ __attribute__((aligned(1024))) char v_lds0[Cfg::TILE];
     __shared__ __attribute__((aligned(1024))) char v_lds1[Cfg::TILE];
-    FA_LDS char* const kbuf[2] = {(FA_LDS char*)k_lds0, (FA_LDS char*)k_lds1};
-    FA_LDS char* const vbuf[2] = {(FA_LDS char*)v_lds0, (FA_LDS char*)v_lds1};
+    FA_LDS char* const kbuf[2] = {(FA_LDS char*)k_lds0, SINGLE ? (FA_LDS char*)k_lds0 : (FA_LDS char*)k_lds1};
+    FA_LDS char* const vbuf[2] = {(FA_LDS char*)v_lds0, SINGLE ? (FA_LDS char*)v_lds0 : (FA_LDS char*)v_lds1};
+    // K(0): the last slot of the second K array in either mode
+    FA_LDS char* const k0slot = (FA_LDS char*)k_lds1 + (SUB - 1) * BN * RB;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -233,7 +241,7 @@ void fa_fwd_split_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
         constexpr int K0_LOADS = BN * RB / 1024;  // 1 KiB transfers of K(0)
         static_assert(K0_LOADS <= Cfg::NW, "K(0) in one transfer per wave");
         if (wave < K0_LOADS)
-            load_part<T, Cfg>(kbuf[1] + (SUB - 1) * BN * RB + wave * 1024, krs, koff, 0);
+            load_part<T, Cfg>(k0slot + wave * 1024, krs, koff, 0);
     }
     load_tile<T, Cfg, false>(kbuf[0], krs, koff, BN, wave, lane);
     load_tile<T, Cfg, true>(vbuf[0], vrs, voff, 0, wave, lane);
@@ -277,7 +285,7 @@ void fa_fwd_split_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
 
     wait_vmcnt0();
     __syncthreads();
-    ST::read_k(kbuf[1] + (SUB - 1) * BN * RB, offk, kfr);
+    ST::read_k(k0slot, offk, kfr);
     if (wt[0] > 0) ST::qk(kfr, qf[0], s[0]);
 
     // Generic half-step (first tile, masked tiles, a block's last tiles): the
@@ -331,7 +339,16 @@ void fa_fwd_split_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
         ST::read_k(kc + u * BN * RB, offk, kfr);
         ST::read_v(vc + u * BN * RB, offv, vfr);
         __builtin_amdgcn_sched_barrier(0);
-        if (u == 0 && j + 1 < nlds) {
+        if constexpr (SINGLE) {
+            // one buffer: refill it only once every wave has read its last slot
+            if (u == SUB - 1) {
+                __syncthreads();
+                if (j + 1 < nlds) {
+                    load_tile<T, Cfg, false>(kn, krs, koff, (j + 1) * Cfg::TBN + BN, wave, lane);
+                    load_tile<T, Cfg, true>(vn, vrs, voff, (j + 1) * Cfg::TBN, wave, lane);
+                }
+            }
+        } else if (u == 0 && j + 1 < nlds) {
             load_tile<T, Cfg, false>(kn, krs, koff, (j + 1) * Cfg::TBN + BN, wave, lane);
             load_tile<T, Cfg, true>(vn, vrs, voff, (j + 1) * Cfg::TBN, wave, lane);
         }

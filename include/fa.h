@@ -54,6 +54,7 @@ extern "C" {
 #define FA_ERR_ALIGNMENT 10     /* a [B,H,S,D] tensor not 16-byte aligned, or lse / delta not 4-byte aligned */
 #define FA_ERR_WINDOW 11        /* a window bound is below -1 */
 #define FA_ERR_WORKSPACE 12     /* fa_bwd_noalloc: B * H * S_q exceeds its static workspace */
+#define FA_ERR_UNSUPPORTED 13   /* fa_fwd_single_buffered: no single-buffered variant for this problem */
 
 /* ---- element types (the dtype argument) --------------------------------- */
 #define FA_DTYPE_F32 0
@@ -183,6 +184,28 @@ int fa_bwd_ex(const void *q, const void *k, const void *v, const void *o, const 
               int64_t B, int64_t H, int64_t H_kv, int64_t S_q, int64_t S_k, int64_t D,
               int causal, int64_t window_left, int64_t window_right,
               float scale, int dtype, void *stream);
+
+/*
+ * fa_fwd_single_buffered -- race check of the forward's double-buffered K/V
+ * staging (a test entry point, not a faster path): fa_fwd computed by the same
+ * two-block kernel with one K and one V LDS buffer, each tile's HBM -> LDS
+ * transfers issued only after a barrier that follows every wave's last read
+ * of the previous tile.  Same arithmetic in the same order, so O and lse must
+ * equal fa_fwd's bit for bit; a difference exposes a read of a buffer while a
+ * transfer refills it.  (Double buffering of the K/V tiles: "T5 讲解：
+ * FlashAttention forward", section ③; "Triton 实现", section "内层循环",
+ * num_stages.)
+ *
+ *   arguments as for fa_fwd.
+ *
+ * Exists for the problems fa_fwd runs on that kernel: dtype fp16 or bf16,
+ * D = 32 or 64, B * H * ceil(S / 256) >= 512.  Any other problem returns
+ * FA_ERR_UNSUPPORTED before any HIP call (after the argument checks of
+ * fa_fwd, whose codes come first).
+ */
+int fa_fwd_single_buffered(const void *q, const void *k, const void *v, void *o, float *lse,
+                           int64_t B, int64_t H, int64_t S, int64_t D,
+                           int causal, float scale, int dtype, void *stream);
 
 /*
  * fa_bwd_noalloc -- fa_bwd_ex without the delta workspace argument, for callers

@@ -297,3 +297,15 @@ def test_bwd_noalloc_rejects_oversized_problem(fa):
     st = fa.fa_bwd_noalloc(P, 2 * P, 3 * P, 4 * P, 5 * P, 6 * P, 7 * P, 8 * P, 9 * P, 1, 1, 1, 4194305, 64, 48,
                            0, -1, -1, 0.125, fa.FA_DTYPE_F16, 0)
     assert st == fa.FA_ERR_HEAD_DIM
+
+
+@pytest.mark.parametrize("over", [dict(dtype=0), dict(D=16), dict(D=128), dict(B=1, H=1, S=64)])
+def test_single_buffered_unsupported_problems(fa, over):
+    """The race-check entry exists only where fa_fwd runs the two-block kernel;
+    elsewhere it returns FA_ERR_UNSUPPORTED before any HIP call."""
+    G = 1 << 32  # fake, never-dereferenced buffers far enough apart not to overlap
+    a = dict(ARGS, q=G, k=2 * G, v=3 * G, o=4 * G, lse=5 * G, B=4, H=16, S=4096, D=64)
+    a.update(over)
+    st = fa.fa_fwd_single_buffered(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["S"], a["D"],
+                                   a["causal"], a["scale"], a["dtype"], a["stream"])
+    assert st == fa.FA_ERR_UNSUPPORTED
