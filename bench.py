@@ -8,9 +8,10 @@ attention-forward TFLOP/s with FLOPs = 4*B*H*S^2*D, halved for causal, and its
 fraction of the MI355X dense fp16 matrix peak (2.5 PFLOP/s).
 
 Prints one JSON line.  Also reported:
-  roofline      (mfma_busy_pct: SQ_VALU_MFMA_BUSY_CYCLES against the kernel's
-                cycles, from the committed rocprofv3 summary while the sources
-                match)
+  roofline      (mfma_busy_pct, valu_active_pct: SQ_VALU_MFMA_BUSY_CYCLES and
+                SQ_ACTIVE_INST_VALU against the kernel's SIMD-cycles, from the
+                committed rocprofv3 summary profiles/*_busy.txt of the workload
+                while the sources match)
                 achieved TFLOP/s of the attention kernel from HIP events around
                 every timed launch on the stream it runs on, against the peak;
                 `traffic` is the HBM bytes per launch measured with rocprofv3
@@ -78,22 +79,24 @@ def profiled_traffic(workload):
     return None
 
 
-def profiled_mfma_busy():
-    """MFMA busy % per kernel ({'fwd', 'dq', 'dkdv'}) from the committed rocprofv3
-    summary, or {} when it does not match the current kernel sources."""
+def profiled_busy(workload):
+    """MFMA busy % and VALU active % per kernel ({'mfma_busy_pct_fwd': ..,
+    'valu_active_pct_dq': .., ...}) from the committed rocprofv3 summary
+    profiles/*_busy.txt of this workload, or {} when none matches the current
+    kernel sources."""
+    import glob
     from exact_tiled_attention_06_amd import build
-    path = os.path.join(ROOT, "profiles", "fa_f16_d64_causal_b4h16s4096_mfma_busy.txt")
-    if not os.path.exists(path):
-        return {}
-    kv = {}
-    with open(path) as f:
-        for line in f:
-            key, sep, val = line.partition(":")
-            if sep and not line.startswith(" "):
-                kv[key.strip()] = val.strip()
-    if kv.get("source_sha256") != build.source_hash():
-        return {}
-    return {k[len("mfma_busy_pct_"):]: float(v) for k, v in kv.items() if k.startswith("mfma_busy_pct_")}
+    want = build.source_hash()
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*_busy.txt"))):
+        kv = {}
+        with open(path) as f:
+            for line in f:
+                key, sep, val = line.partition(":")
+                if sep and not line.startswith(" "):
+                    kv[key.strip()] = val.strip()
+        if kv.get("workload") == workload and kv.get("source_sha256") == want:
+            return {k: float(v) for k, v in kv.items() if k.startswith(("mfma_busy_pct_", "valu_active_pct_"))}
+    return {}
 
 
 def time_workload(fa, torch, w, causal, steps, warmup):
@@ -411,8 +414,9 @@ def main():
         "cpu_baseline": None,
     }
 
-    busy = profiled_mfma_busy() if w.name == "multihead_causal" else {}
-    out["roofline"]["mfma_busy_pct"] = busy.get("fwd")
+    busy = profiled_busy(w.name)
+    out["roofline"]["mfma_busy_pct"] = busy.get("mfma_busy_pct_fwd")
+    out["roofline"]["valu_active_pct"] = busy.get("valu_active_pct_fwd")
 
     if not args.no_backward and w.dtype in ("f16", "bf16"):
         bwall, bms = time_backward(fa, torch, w, causal, args.steps, args.warmup)
@@ -438,7 +442,10 @@ def main():
                 "traffic_unit": "bytes per fa_bwd call (both kernels; HBM, rocprofv3 FETCH_SIZE + WRITE_SIZE)",
                 "kernel_ms_avg": round(bavg, 5),
                 "kernel_ms_min": round(min(bms), 5),
-                "mfma_busy_pct": {"dq": busy.get("dq"), "dkdv": busy.get("dkdv")} if busy else None,
+                "mfma_busy_pct": {"dq": busy.get("mfma_busy_pct_dq"), "dkdv": busy.get("mfma_busy_pct_dkdv")}
+                                 if busy else None,
+                "valu_active_pct": {"dq": busy.get("valu_active_pct_dq"), "dkdv": busy.get("valu_active_pct_dkdv")}
+                                   if busy else None,
             },
             "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline_backward(w, causal),
         }
