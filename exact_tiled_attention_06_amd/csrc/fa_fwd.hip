@@ -118,9 +118,12 @@ int launch_ksplit(const Fwd& a) {
     const int64_t grid = (int64_t)n_qblk * a.BH;
     if (grid > (int64_t)1 << 24) return FA_ERR_TOO_LARGE;
     (void)hipGetLastError();
+    // a causal grid that fills the compute units at most twice (two workgroups
+    // per unit are resident at once) pairs its rounds long with short
+    const int round = (Cfg::CAUSAL && grid > kCUs && grid <= 2 * kCUs) ? (int)kCUs : 0;
     hipLaunchKernelGGL((fa_fwd_ksplit_kernel<T, Cfg>), dim3((unsigned)grid), dim3(Cfg::NT), 0, a.stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse,
-                       a.Sq, a.Sk, a.BH, n_qblk, a.G, a.c);
+                       a.Sq, a.Sk, a.BH, n_qblk, a.G, a.c, round);
     return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 

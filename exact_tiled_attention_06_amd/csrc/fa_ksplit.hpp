@@ -15,10 +15,13 @@
 // exchange (m, l, acc) through LDS and wave 0 merges and writes O and lse.
 // With NW waves per block, a thin grid gets NW times the waves and each row's
 // serial chain of tiles is NW times shorter, at the same HBM traffic (every
-// block still reads its key range once).
+// block still reads its key range once).  With two 32-row blocks per wave
+// (D = 32, 64) a wave walks its slice with the half-step loop of fa_split.hpp;
+// the arithmetic, and so every output bit, is that of the plain loop.
 #pragma once
 
 #include "fa_mfma.hpp"
+#include "fa_split.hpp"
 
 namespace fa {
 
@@ -48,7 +51,7 @@ template <typename T, typename Cfg>
 __global__ __attribute__((amdgpu_flat_work_group_size(Cfg::NT, Cfg::NT), amdgpu_waves_per_eu(Cfg::OCC, Cfg::OCC)))
 void fa_fwd_ksplit_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                           const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
-                          int Sq, int Sk, int BH, int n_qblk, int G, float c) {
+                          int Sq, int Sk, int BH, int n_qblk, int G, float c, int round) {
     using W = WaveTile<T, Cfg>;
     using L = WaveLoader<Cfg>;
     constexpr int D = Cfg::D, QB = Cfg::QB, KB = Cfg::KB, KS = Cfg::KS, DB = Cfg::DB;
@@ -73,9 +76,17 @@ void fa_fwd_ksplit_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
 
     // Workgroup -> (head, query block): heads vary fastest, causal blocks
     // longest first.  Every wave holds the block's BMW rows.
-    const int wg = blockIdx.x;
-    const int bh = wg % BH;
-    const int rank = wg / BH;
+    // With `round` > 0 (a causal grid of at most two resident rounds of `round`
+    // workgroups, launched one round after the other onto the same compute
+    // units), the second round takes its blocks in the opposite order, so that a
+    // unit that got a long block in the first round gets a short one next.
+    int lin = blockIdx.x;
+    if (CAUSAL && round > 0 && lin >= round && lin < 2 * round) {
+        const int m = min(round, (int)gridDim.x - round);  // second-round workgroups
+        lin = 2 * round + m - 1 - lin;
+    }
+    const int bh = lin % BH;
+    const int rank = lin / BH;
     const int qblk = CAUSAL ? (n_qblk - 1 - rank) : rank;
     const int q0 = qblk * BMW;
 
@@ -133,7 +144,123 @@ void fa_fwd_ksplit_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
             for (int r = 0; r < 16; ++r) oacc[qb][db][r] = 0.f;
     }
 
-    if (nt > 0) {
+    constexpr bool kHalf = QB == 2 && KB == 1 && KS >= 2;
+    if constexpr (kHalf) {
+        // Two 32-row blocks per wave (D = 32, 64): the half-step loop of
+        // fa_split.hpp (softmax of one block beside the other block's MFMAs)
+        // over this wave's slice.  Relative tile u = t - tb: LDS tile u, in
+        // buffers u & 1, holds K(t+1) and V(t); K(tb) waits in the second K
+        // buffer, which LDS tile 1 refills after K(tb)'s fragments were
+        // consumed.  The wave is the only reader of its buffers, so a refill
+        // needs no barrier: the fragments of the tile it replaces fed MFMAs
+        // issued before it.
+        using ST = SplitTile<T, Cfg>;
+        // per block a: na = its tiles in the slice, ua = the slice's leading
+        // tiles that need no mask for any of its rows (may be <= 0)
+        int na[2], ua[2];
+#pragma unroll
+        for (int a = 0; a < 2; ++a) {
+            const int r0 = q0 + 32 * a;
+            const int rend = CAUSAL ? min(r0 + 32, Sk) : Sk;
+            const int wt = r0 < Sq ? min(ntiles, (rend + BN - 1) / BN) : 0;
+            na[a] = max(0, min(te, wt) - tb);
+            ua[a] = min(CAUSAL ? (r0 + 1) / BN : ntiles, Sk / BN) - tb;
+        }
+        const int nw = max(na[0], na[1]);  // = na[1] unless block 1 has no rows
+        if (nw > 0) {
+            f32x16 s[2];
+            u32x4 p[2][2];
+            u32x4 kfr[KS], vfr[2][DB];
+            L::template load<T>(kbuf[1], krs, koff, tb * BN);
+            if (nw > 1) L::template load<T>(kbuf[0], krs, koff, (tb + 1) * BN);
+            L::template load<T>(vbuf[0], vrs, voff, tb * BN);
+            wait_vmcnt0();
+            ST::read_k(kbuf[1], offk, kfr);
+            if (na[0] > 0) ST::qk(kfr, qf[0], s[0]);
+
+            // generic half-step (first tile, masked tiles, a block's last tiles)
+            auto half_any = [&](auto blk, int u) __attribute__((always_inline)) {
+                constexpr int A = decltype(blk)::value, B = 1 - A;
+                const int upv = A == 0 ? u - 1 : u;  // block B's P*V tile
+                const int uqk = A == 0 ? u : u + 1;  // block B's S tile
+                if (upv >= 0 && upv < na[B]) ST::pv(vfr, p[B], oacc[B]);
+                if (uqk < na[B]) ST::qk(kfr, qf[B], s[B]);
+                if (u < na[A]) {
+                    if (u >= ua[A]) ST::mask(s[A], last[A], (tb + u) * BN, h);
+                    if (u == 0) {
+                        m_run[A] = fmaxf(m_run[A], ST::rmax(s[A]) * c);
+                        ST::expo(s[A], m_run[A], c, p[A], l_run[A]);
+                    } else {
+                        float rs;
+                        ST::expo(s[A], m_run[A], c, p[A], rs);
+                        if (ST::needs_rescale(rs)) ST::rescale(s[A], m_run[A], l_run[A], oacc[A], c, p[A], rs);
+                        l_run[A] += rs;
+                    }
+                }
+            };
+            auto steady_half = [&](auto blk) __attribute__((always_inline)) {
+                constexpr int A = decltype(blk)::value, B = 1 - A;
+                float rs;
+                ST::half(kfr, vfr, qf[B], s[A], s[B], p[A], p[B], oacc[B], m_run[A], c, rs);
+                if (ST::needs_rescale(rs)) ST::rescale(s[A], m_run[A], l_run[A], oacc[A], c, p[A], rs);
+                l_run[A] += rs;
+            };
+            // between the half-steps of tile u: wait for LDS tile u, read the
+            // fragments of K(t+1) and V(t), then start LDS tile u+1 into the
+            // other buffers (fenced, as in fa_split.hpp, so that no fragment
+            // read moves across the transfers or into another half-step)
+            auto sync_with = [&](int u, FA_LDS char* kc, FA_LDS char* vc, FA_LDS char* kn, FA_LDS char* vn)
+                                 __attribute__((always_inline)) {
+                wait_vmcnt0();
+                __builtin_amdgcn_sched_barrier(0);
+                ST::read_k(kc, offk, kfr);
+                ST::read_v(vc, offv, vfr);
+                __builtin_amdgcn_sched_barrier(0);
+                if (u + 1 < nw) {
+                    if (u + 2 < nw) L::template load<T>(kn, krs, koff, (tb + u + 2) * BN);
+                    L::template load<T>(vn, vrs, voff, (tb + u + 1) * BN);
+                }
+            };
+            auto sync = [&](auto par, int u) __attribute__((always_inline)) {
+                constexpr int P = decltype(par)::value;
+                sync_with(u, kbuf[P], vbuf[P], kbuf[1 - P], vbuf[1 - P]);
+            };
+            auto sync_rt = [&](int u) __attribute__((always_inline)) {
+                const bool odd = u & 1;
+                sync_with(u, odd ? kbuf[1] : kbuf[0], odd ? vbuf[1] : vbuf[0], odd ? kbuf[0] : kbuf[1],
+                          odd ? vbuf[0] : vbuf[1]);
+            };
+            using A0 = std::integral_constant<int, 0>;
+            using A1 = std::integral_constant<int, 1>;
+            // steady for 1 <= u < us: both blocks unmasked, every MFMA present
+            const int us = min(min(ua[0], ua[1]), min(na[1], na[0] - 1));
+            half_any(A0{}, 0);
+            sync_rt(0);
+            half_any(A1{}, 0);
+            int u = 1;
+            for (; u + 1 < us; u += 2) {
+                steady_half(A0{});
+                sync(A1{}, u);
+                steady_half(A1{});
+                steady_half(A0{});
+                sync(A0{}, u + 1);
+                steady_half(A1{});
+            }
+            if (u < us) {
+                steady_half(A0{});
+                sync(A1{}, u);
+                steady_half(A1{});
+                ++u;
+            }
+            for (; u < nw; ++u) {
+                half_any(A0{}, u);
+                sync_rt(u);
+                half_any(A1{}, u);
+            }
+            // P*V of block 1's last tile (its V is still in vfr)
+            if (na[1] == nw) ST::pv(vfr, p[1], oacc[1]);
+        }
+    } else if (nt > 0) {
         // Relative tile u = t - tb lives in buffers u & 1.  Iteration u: S(u) in
         // s_cur, S(u+1) to s_nxt, P(u-1) in p_prv, P(u) to p_cur; K(u+2) and V(u)
         // start into the buffers K(u) and V(u-2) left (their reads ended in
