@@ -15,7 +15,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SOURCES = [os.path.join(HERE, "csrc", "fa_fwd.hip")]
-HEADERS = [os.path.join(HERE, "csrc", f) for f in ("fa_common.hpp", "fa_mfma.hpp", "fa_split.hpp", "fa_ksplit.hpp", "fa_f32.hpp", "fa_bwd.hpp", "fa_window.hpp", "fa_split_window.hpp")] + [
+HEADERS = [os.path.join(HERE, "csrc", f) for f in ("fa_common.hpp", "fa_mfma.hpp", "fa_split.hpp", "fa_ksplit.hpp", "fa_f32m.hpp", "fa_bwd.hpp", "fa_window.hpp", "fa_split_window.hpp")] + [
     os.path.join(ROOT, "include", "fa.h")]
 LIBRARY = os.path.join(HERE, "libfa.so")
 # the instruction-rate microbenchmarks (a measurement tool, separate library)

@@ -14,7 +14,7 @@
 #include <hip/hip_runtime.h>
 
 #include "../../include/fa.h"
-#include "fa_f32.hpp"
+#include "fa_f32m.hpp"
 #include "fa_mfma.hpp"
 #include "fa_ksplit.hpp"
 #include "fa_split.hpp"
@@ -180,13 +180,14 @@ int launch_mfma(const Fwd& a) {
     }
 }
 
+// fp32: workgroups of 32 query rows on the fp32 matrix cores
 template <int D, bool CAUSAL>
 int launch_f32(const Fwd& a) {
-    const int n_qblk = (a.Sq + F32_BM - 1) / F32_BM;
+    const int n_qblk = (a.Sq + 31) / 32;
     const int64_t grid = (int64_t)n_qblk * a.BH;
     if (grid > (int64_t)1 << 24) return FA_ERR_TOO_LARGE;
     (void)hipGetLastError();
-    hipLaunchKernelGGL((fa_fwd_f32_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(F32Cfg<D>::NT), 0, a.stream,
+    hipLaunchKernelGGL((fa_fwd_f32m_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(F32mCfg<D>::NT), 0, a.stream,
                        (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.o, a.lse, a.Sq, a.Sk,
                        a.BH, n_qblk, a.G, a.wl, a.wr, a.c);
     return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
