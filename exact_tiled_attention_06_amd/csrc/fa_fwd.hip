@@ -94,6 +94,26 @@ int fill_words(void* p, uint32_t value, int64_t bytes, hipStream_t stream) {
     return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
+// The `round` argument of the two-block and key-split kernels.  When two of
+// their 4-wave workgroups fit on a compute unit (two waves per SIMD, and LDS
+// for two), a causal grid of more than one and at most two rounds of kCUs
+// workgroups is resident all at once, workgroup i + kCUs on the unit of
+// workgroup i, and pairs its rounds long with short.  Otherwise (0) the order
+// stays longest first: the hardware then starts each later workgroup on the
+// first unit to free up, which balances by itself.  Measured on B=8 H=1,
+// causal: the key-split kernel gains at D = 32 and 64 (S=4096 D=64 32.0 ->
+// 27.8 us) and the two-block kernel at D = 32 (S=16384 244.5 -> 215.8 us), but
+// the two-block kernel at D = 64 loses (S=16384 314.0 -> 335.2 us): there the
+// time is the longest block's own chain of tiles, which runs faster beside a
+// second, lower-priority wave on its SIMDs than alone (1286 against 1340
+// cycles per tile in per-wave timestamps), so it keeps longest first.
+template <typename Cfg, int LDS_BYTES, bool SPLIT>
+int two_round_order(int64_t grid) {
+    constexpr bool two_per_cu = Cfg::NW == 4 && Cfg::OCC == 2 && Cfg::D <= 64 && 2 * LDS_BYTES <= 160 * 1024;
+    constexpr bool gains = !SPLIT || Cfg::D <= 32;
+    return (two_per_cu && gains && Cfg::CAUSAL && grid > kCUs && grid <= 2 * kCUs) ? (int)kCUs : 0;
+}
+
 template <typename T, typename Cfg, bool SINGLE = false>
 int launch_cfg(const Fwd& a) {
     const int n_qblk = (a.Sq + Cfg::BM - 1) / Cfg::BM;
@@ -103,7 +123,7 @@ int launch_cfg(const Fwd& a) {
     if constexpr (Cfg::QB == 2 && Cfg::KB == 1 && Cfg::PIPE)
         hipLaunchKernelGGL((fa_fwd_split_kernel<T, Cfg, SINGLE>), dim3((unsigned)grid), dim3(Cfg::NT), 0, a.stream,
                            (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o,
-                           a.lse, a.Sq, a.Sk, a.BH, n_qblk, a.G, a.c);
+                           a.lse, a.Sq, a.Sk, a.BH, n_qblk, a.G, a.c, two_round_order<Cfg, 4 * Cfg::TILE, true>(grid));
     else
         hipLaunchKernelGGL((fa_fwd_mfma_kernel<T, Cfg>), dim3((unsigned)grid), dim3(Cfg::NT), 0, a.stream,
                            (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o,
@@ -118,12 +138,9 @@ int launch_ksplit(const Fwd& a) {
     const int64_t grid = (int64_t)n_qblk * a.BH;
     if (grid > (int64_t)1 << 24) return FA_ERR_TOO_LARGE;
     (void)hipGetLastError();
-    // a causal grid that fills the compute units at most twice (two workgroups
-    // per unit are resident at once) pairs its rounds long with short
-    const int round = (Cfg::CAUSAL && grid > kCUs && grid <= 2 * kCUs) ? (int)kCUs : 0;
     hipLaunchKernelGGL((fa_fwd_ksplit_kernel<T, Cfg>), dim3((unsigned)grid), dim3(Cfg::NT), 0, a.stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse,
-                       a.Sq, a.Sk, a.BH, n_qblk, a.G, a.c, round);
+                       a.Sq, a.Sk, a.BH, n_qblk, a.G, a.c, two_round_order<Cfg, ksplit_lds_bytes<Cfg>(), false>(grid));
     return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 

@@ -47,6 +47,19 @@ struct WaveLoader {
     }
 };
 
+// LDS of one workgroup: per wave two K and two V tiles.  After the loop the
+// same memory holds the exchange of waves 1..NW-1: per lane QB*DB*16
+// accumulators, QB m, QB l.
+template <typename Cfg>
+constexpr int ksplit_xch_bytes() {
+    return (Cfg::QB * Cfg::DB * 16 + 2 * Cfg::QB) * 64 * 4;  // per wave
+}
+template <typename Cfg>
+constexpr int ksplit_lds_bytes() {
+    return Cfg::NW * 4 * Cfg::TILE > (Cfg::NW - 1) * ksplit_xch_bytes<Cfg>() ? Cfg::NW * 4 * Cfg::TILE
+                                                                               : (Cfg::NW - 1) * ksplit_xch_bytes<Cfg>();
+}
+
 template <typename T, typename Cfg>
 __global__ __attribute__((amdgpu_flat_work_group_size(Cfg::NT, Cfg::NT), amdgpu_waves_per_eu(Cfg::OCC, Cfg::OCC)))
 void fa_fwd_ksplit_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
@@ -59,11 +72,7 @@ void fa_fwd_ksplit_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     constexpr bool CAUSAL = Cfg::CAUSAL;
     static_assert(Cfg::PIPE && Cfg::TBN == BN, "pipelined loop, one compute tile per LDS tile");
 
-    // Per wave: two K and two V tiles.  After the loop the same memory holds
-    // the exchange of waves 1..NW-1: per lane QB*DB*16 accumulators, QB m, QB l.
-    constexpr int XCH = (QB * DB * 16 + 2 * QB) * 64 * 4;  // bytes per wave
-    constexpr int LDS_BYTES = NW * 4 * TILE > (NW - 1) * XCH ? NW * 4 * TILE : (NW - 1) * XCH;
-    __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
+    __shared__ __attribute__((aligned(1024))) char lds[ksplit_lds_bytes<Cfg>()];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -76,15 +85,7 @@ void fa_fwd_ksplit_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
 
     // Workgroup -> (head, query block): heads vary fastest, causal blocks
     // longest first.  Every wave holds the block's BMW rows.
-    // With `round` > 0 (a causal grid of at most two resident rounds of `round`
-    // workgroups, launched one round after the other onto the same compute
-    // units), the second round takes its blocks in the opposite order, so that a
-    // unit that got a long block in the first round gets a short one next.
-    int lin = blockIdx.x;
-    if (CAUSAL && round > 0 && lin >= round && lin < 2 * round) {
-        const int m = min(round, (int)gridDim.x - round);  // second-round workgroups
-        lin = 2 * round + m - 1 - lin;
-    }
+    const int lin = CAUSAL ? causal_work_index(round, BH) : (int)blockIdx.x;
     const int bh = lin % BH;
     const int rank = lin / BH;
     const int qblk = CAUSAL ? (n_qblk - 1 - rank) : rank;

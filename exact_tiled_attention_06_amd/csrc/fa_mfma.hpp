@@ -196,6 +196,27 @@ __device__ __forceinline__ void load_part(FA_LDS char* dst, __amdgpu_buffer_rsrc
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (FA_LDS void*)dst, 16, lane_off + (uint32_t)(k0 * Cfg::RB), 0, 0, 0);
 }
 
+// Work order of a causal grid whose workgroups are longest first, heads
+// fastest (position p: head p % BH, rank p / BH).  With `round` > 0 (a grid of
+// at most two resident rounds of `round` workgroups: all of it fits on the GPU
+// at once, and workgroup i + round lands on the compute unit of workgroup i),
+// the second round takes its blocks in the opposite order, so that a unit that
+// got a long block in the first round gets a short one next.  When BH divides
+// both rounds, only the ranks are reversed and every workgroup keeps its head,
+// so a head's workgroups stay on the XCD (and L2) the plain order gives them.
+// Returns this workgroup's position in the longest-first order.
+__device__ __forceinline__ int causal_work_index(int round, int BH) {
+    int lin = blockIdx.x;
+    if (round > 0 && lin >= round && lin < 2 * round) {
+        const int m = min(round, (int)gridDim.x - round);  // second-round workgroups
+        if (round % BH == 0 && m % BH == 0)
+            lin = round + (m / BH - 1 - (lin - round) / BH) * BH + lin % BH;
+        else
+            lin = 2 * round + m - 1 - lin;
+    }
+    return lin;
+}
+
 // Per-wave state and the pieces of work on one tile.
 template <typename T, typename Cfg>
 struct WaveTile {

@@ -174,7 +174,7 @@ template <typename T, typename Cfg, bool SINGLE = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(Cfg::NT, Cfg::NT), amdgpu_waves_per_eu(Cfg::OCC, Cfg::OCC)))
 void fa_fwd_split_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                          const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE, int Sq, int Sk,
-                         int BH, int n_qblk, int G, float c) {
+                         int BH, int n_qblk, int G, float c, int round) {
     using ST = SplitTile<T, Cfg>;
     constexpr int D = Cfg::D, KS = Cfg::KS, DB = Cfg::DB;
     constexpr int BN = Cfg::BN, BM = Cfg::BM, BMW = Cfg::BMW, RB = Cfg::RB;
@@ -206,7 +206,7 @@ void fa_fwd_split_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
 
     // Workgroup -> (head, query block): heads vary fastest (one head's blocks
     // share an XCD's L2), causal blocks longest first.
-    const int wg = blockIdx.x;
+    const int wg = CAUSAL ? causal_work_index(round, BH) : (int)blockIdx.x;
     const int bh = wg % BH;
     const int rank = wg / BH;
     const int qblk = CAUSAL ? (n_qblk - 1 - rank) : rank;
