@@ -395,6 +395,18 @@ struct WaveTile {
 #pragma unroll
             for (; nc < c_end; ++nc) pair_pack(x[nc], nc, p_cur, rs);
         }
+        if constexpr (Cfg::D == 128 && QB == 1 && KB == 1) {
+            // D = 128, 32-key steps: the issue order pinned by scheduling
+            // groups, four vector instructions first, then every MFMA followed
+            // by three of them (measured 1-8 % faster than the compiler's
+            // order; lead 8, or four per MFMA, gained less)
+            __builtin_amdgcn_sched_group_barrier(kSchedValu, 4, 0);
+#pragma unroll
+            for (int i = 0; i < NM; ++i) {
+                __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(kSchedValu, 3, 0);
+            }
+        }
     }
 
     // True when some lane's partial sum of this tile is out of range (or inf).
