@@ -351,6 +351,10 @@ struct WaveTile {
     // scores exponentiated while they are in flight, then every MFMA followed by
     // its share of the softmax -- and left to the compiler's scheduler (pinning
     // the order measured slower).  Same arithmetic as qk + pv + expo.
+    // PIN_ORDER: pin the issue order at D = 128 (the one-block kernel; the
+    // key-split kernel, whose D = 128 instance runs one wave per SIMD, measured
+    // slower with it: B=8 H=1 S=1024 12.3 -> 14.0 us)
+    template <bool PIN_ORDER = false>
     static __device__ __forceinline__ void step(const FA_LDS char* kn, const FA_LDS char* vp, const int (&offk)[KS],
                                                 const int (&offv)[DB], const u32x4 (&qf)[QB][KS],
                                                 const f32x16 (&s_cur)[QB][KB], f32x16 (&s_nxt)[QB][KB],
@@ -395,7 +399,7 @@ struct WaveTile {
 #pragma unroll
             for (; nc < c_end; ++nc) pair_pack(x[nc], nc, p_cur, rs);
         }
-        if constexpr (Cfg::D == 128 && QB == 1 && KB == 1) {
+        if constexpr (PIN_ORDER && Cfg::D == 128 && QB == 1 && KB == 1) {
             // D = 128, 32-key steps: the issue order pinned by scheduling
             // groups, four vector instructions first, then every MFMA followed
             // by three of them (measured 1-8 % faster than the compiler's
@@ -609,7 +613,7 @@ void fa_fwd_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
             }
             float rs[QB];
             if constexpr (KIND == 1) {
-                W::step(kn, vp, offk, offv, qf, s_cur, s_nxt, p_prv, p_cur, oacc, m_run, c, rs);
+                W::template step<true>(kn, vp, offk, offv, qf, s_cur, s_nxt, p_prv, p_cur, oacc, m_run, c, rs);
             } else {
                 const bool do_qk = t + 1 < wtiles;
                 const bool do_pv = t <= wtiles;
