@@ -123,20 +123,24 @@ def time_workload(fa, torch, w, causal, steps, warmup):
 
 
 def time_graph(fa, torch, w, causal, launches=20, reps=10):
-    """Kernel time per launch from a HIP graph of `launches` fa_fwd_ex calls on
+    """Time per forward from a HIP graph of `launches` fa_fwd_ws calls (with the
+    workspace fa_fwd_workspace_bytes asks for, as forward() passes it) on
     preallocated buffers, replayed `reps` times between two events: the GPU
     never waits for the host, so short kernels are timed without the Python
-    call's overhead.  Returns the milliseconds per launch."""
+    call's overhead.  Returns the milliseconds per forward."""
     import workloads
     q, k, v = (x.to("cuda:0") for x in workloads.workload_inputs(w))
     o = torch.empty_like(q)
     lse = torch.empty((w.B, w.H, w.S), dtype=torch.float32, device="cuda:0")
     wl, wr = w.window
     code = fa.DTYPE_CODES[q.dtype]
+    nbytes = fa.fa_fwd_workspace_bytes(w.B, w.H, k.shape[1], w.S, w.S, w.D, int(causal), wl, wr, code)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda:0")
 
     def call(stream):
-        return fa.fa_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), w.B, w.H,
-                            k.shape[1], w.S, w.S, w.D, int(causal), wl, wr, w.scale, code, stream)
+        return fa.fa_fwd_ws(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), w.B, w.H,
+                            k.shape[1], w.S, w.S, w.D, int(causal), wl, wr, w.scale, code, ws.data_ptr(), nbytes,
+                            stream)
 
     side = torch.cuda.Stream()
     with torch.cuda.stream(side):

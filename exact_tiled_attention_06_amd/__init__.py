@@ -15,12 +15,16 @@ import this package before the library exists.
         the C status description;
     forward(q, k, v, causal=False, scale=None, window=None) -> (o, lse)
         convenience on torch tensors q [B,H,S_q,D], k and v [B,H_kv,S_k,D]:
-        allocates o (input dtype) and lse (float32 [B,H,S_q]) and calls
-        fa_fwd_ex on the current stream.  The default scale is 1/sqrt(D)
+        allocates o (input dtype), lse (float32 [B,H,S_q]) and the workspace
+        fa_fwd_workspace_bytes asks for (none for most problems) and calls
+        fa_fwd_ws on the current stream.  The default scale is 1/sqrt(D)
         ("T5 讲解：FlashAttention forward", section ⑥).
     fa_fwd_ex / fa_bwd_ex(...)
         the C entry points with grouped K/V heads (H_kv), separate query and
         key lengths (S_q, S_k) and a sliding window;
+    fa_fwd_workspace_bytes(...), fa_fwd_ws(...)
+        the workspace the forward uses to split the longest causal query
+        blocks over two workgroups, and fa_fwd_ex with that workspace;
     fa_fwd_single_buffered(...)
         race check: fa_fwd's two-block kernel with single-buffered K/V staging;
     fa_bwd_noalloc(...)
@@ -85,6 +89,10 @@ def _load() -> ctypes.CDLL:
     lib.fa_fwd_ex.argtypes = [P] * 5 + [I64] * 6 + [I, I64, I64, F, I, P]
     lib.fa_bwd_ex.restype = I
     lib.fa_bwd_ex.argtypes = [P] * 10 + [I64] * 6 + [I, I64, I64, F, I, P]
+    lib.fa_fwd_workspace_bytes.restype = I64
+    lib.fa_fwd_workspace_bytes.argtypes = [I64] * 6 + [I, I64, I64, I]
+    lib.fa_fwd_ws.restype = I
+    lib.fa_fwd_ws.argtypes = [P] * 5 + [I64] * 6 + [I, I64, I64, F, I, P, I64, P]
     lib.fa_fwd_single_buffered.restype = I
     lib.fa_fwd_single_buffered.argtypes = [P] * 5 + [I64] * 4 + [I, F, I, P]
     lib.fa_bwd_noalloc.restype = I
@@ -142,6 +150,24 @@ def fa_fwd_ex(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, H_kv: in
     sliding window; returns the status code."""
     return int(library().fa_fwd_ex(q, k, v, o, lse, B, H, H_kv, S_q, S_k, D, int(causal), int(window_left),
                                    int(window_right), float(scale), int(dtype), stream))
+
+
+def fa_fwd_workspace_bytes(B: int, H: int, H_kv: int, S_q: int, S_k: int, D: int, causal: int,
+                           window_left: int, window_right: int, dtype: int) -> int:
+    """Bytes of the workspace with which fa_fwd_ws splits the longest causal
+    query blocks over two workgroups; 0 when the problem runs without one."""
+    return int(library().fa_fwd_workspace_bytes(B, H, H_kv, S_q, S_k, D, int(causal), int(window_left),
+                                                int(window_right), int(dtype)))
+
+
+def fa_fwd_ws(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, H_kv: int, S_q: int, S_k: int,
+              D: int, causal: int, window_left: int, window_right: int, scale: float, dtype: int,
+              workspace: int, workspace_bytes: int, stream: int) -> int:
+    """fa_fwd_ex with a caller-given device workspace (see fa_fwd_workspace_bytes);
+    returns the status code."""
+    return int(library().fa_fwd_ws(q, k, v, o, lse, B, H, H_kv, S_q, S_k, D, int(causal), int(window_left),
+                                   int(window_right), float(scale), int(dtype), workspace, int(workspace_bytes),
+                                   stream))
 
 
 def fa_bwd_ex(q: int, k: int, v: int, o: int, dout: int, lse: int, dq: int, dk: int, dv: int, delta: int,
@@ -232,9 +258,14 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = Fa
         raise ValueError(f"out and lse must be on q's device {q.device}; got {out.device}, {lse.device}")
     stream = torch.cuda.current_stream(q.device).cuda_stream
     wl, wr = _window(window)
-    status = fa_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                       B, H, k.shape[1], S, S_k, D, int(bool(causal)), wl, wr, scale, DTYPE_CODES[q.dtype],
-                       stream)
+    code = DTYPE_CODES[q.dtype]
+    # the workspace of the key split of the longest causal blocks (0 bytes for
+    # most problems: then this is fa_fwd_ex)
+    nbytes = fa_fwd_workspace_bytes(B, H, k.shape[1], S, S_k, D, int(bool(causal)), wl, wr, code)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device) if nbytes > 0 else None
+    status = fa_fwd_ws(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                       B, H, k.shape[1], S, S_k, D, int(bool(causal)), wl, wr, scale, code,
+                       ws.data_ptr() if ws is not None else 0, nbytes, stream)
     check(status)
     return out, lse
 

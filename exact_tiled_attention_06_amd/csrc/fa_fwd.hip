@@ -79,6 +79,8 @@ struct Fwd {
     float c;            // scale * log2(e)
     hipStream_t stream;
     bool single;        // race check: the single-buffered two-block kernel
+    void* ws;           // caller's workspace for the key split of the longest blocks (or NULL)
+    int64_t ws_bytes;
 };
 
 // Fills n 32-bit words with `value` (outputs of problems without keys or
@@ -96,6 +98,25 @@ int fill_words(void* p, uint32_t value, int64_t bytes, hipStream_t stream) {
     hipLaunchKernelGGL(fa_fill_kernel, dim3((unsigned)(blocks < 4096 ? blocks : 4096)), dim3(256), 0, stream,
                        (uint32_t*)p, value, n);
     return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+// Workspace for the key split of the longest blocks (fa_fwd_split_kernel with
+// nsplit > 0), 0 when the problem does not use it.  The split pays where the
+// two-block kernel's whole grid is resident at once (at most 2 * kCUs
+// workgroups of 256 rows; it is used from kFullGrid = 2 * kCUs up, so exactly
+// that many): there the longest blocks' serial chains of tiles set the time
+// (per-wave timestamps: the longest block runs 30 % longer than the mean
+// load of a compute unit).  The n_qblk / 2 longest blocks of every head then
+// run as two key halves each, with an fp32 partial of 256 rows x (D + 1)
+// values per half.  Causal, no window, D = 32 or 64 (the two-block kernel),
+// S_q = S_k (every row of a split block then sees keys in both halves).
+int64_t split_workspace_bytes(int64_t D, bool causal, int wl, int wr, int64_t Sq, int64_t Sk, int64_t BH) {
+    constexpr int64_t kBM = 256;  // rows per two-block workgroup (4 waves x 64)
+    if (!causal || wl >= 0 || wr >= 0 || (D != 32 && D != 64) || Sq != Sk) return 0;
+    const int64_t n_qblk = (Sq + kBM - 1) / kBM;
+    const int64_t grid = n_qblk * BH;
+    if (grid < kFullGrid || grid > 2 * kCUs || n_qblk < 2) return 0;
+    return (n_qblk / 2) * BH * 2 * kBM * (D + 1) * 4;
 }
 
 // The `round` argument of the two-block and key-split kernels.  When two of
@@ -124,14 +145,35 @@ int launch_cfg(const Fwd& a) {
     const int64_t grid = (int64_t)n_qblk * a.BH;
     if (grid > (int64_t)1 << 24) return FA_ERR_TOO_LARGE;
     (void)hipGetLastError();  // clear a stale error so the check below sees this launch only
-    if constexpr (Cfg::QB == 2 && Cfg::KB == 1 && Cfg::PIPE)
-        hipLaunchKernelGGL((fa_fwd_split_kernel<T, Cfg, SINGLE>), dim3((unsigned)grid), dim3(Cfg::NT), 0, a.stream,
+    if constexpr (Cfg::QB == 2 && Cfg::KB == 1 && Cfg::PIPE) {
+        // the key split of the longest blocks, when the caller's workspace holds it
+        int nsplit = 0;
+        float *po = nullptr, *pl = nullptr;
+        if constexpr (!SINGLE) {
+            const int64_t need = split_workspace_bytes(Cfg::D, Cfg::CAUSAL, a.wl, a.wr, a.Sq, a.Sk, a.BH);
+            if (need > 0 && a.ws && a.ws_bytes >= need) {
+                nsplit = n_qblk / 2;
+                po = (float*)a.ws;
+                pl = po + (int64_t)nsplit * a.BH * 2 * Cfg::BM * Cfg::D;
+            }
+        }
+        const int64_t g = grid + (int64_t)nsplit * a.BH;  // each split block: two workgroups
+        hipLaunchKernelGGL((fa_fwd_split_kernel<T, Cfg, SINGLE>), dim3((unsigned)g), dim3(Cfg::NT), 0, a.stream,
                            (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o,
-                           a.lse, a.Sq, a.Sk, a.BH, n_qblk, a.G, a.c, two_round_order<Cfg, 4 * Cfg::TILE, true>(grid));
-    else
+                           a.lse, a.Sq, a.Sk, a.BH, n_qblk, a.G, a.c,
+                           nsplit ? 0 : two_round_order<Cfg, 4 * Cfg::TILE, true>(grid), po, pl, nsplit);
+        if (nsplit) {
+            if (hipGetLastError() != hipSuccess) return FA_ERR_LAUNCH;
+            const int64_t threads = (int64_t)nsplit * a.BH * Cfg::BM * (Cfg::D / 4);
+            hipLaunchKernelGGL((fa_fwd_merge_kernel<T, Cfg::D, Cfg::BM>), dim3((unsigned)((threads + 255) / 256)),
+                               dim3(256), 0, a.stream, (const float*)po, (const float*)pl, (uint16_t*)a.o, a.lse,
+                               a.Sq, a.BH, n_qblk, nsplit);
+        }
+    } else {
         hipLaunchKernelGGL((fa_fwd_mfma_kernel<T, Cfg>), dim3((unsigned)grid), dim3(Cfg::NT), 0, a.stream,
                            (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o,
                            a.lse, a.Sq, a.Sk, a.BH, n_qblk, a.G, a.c);
+    }
     return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
@@ -468,10 +510,11 @@ extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o
 
 namespace {
 
-// fa_fwd_ex's work; `single` selects the single-buffered race-check variant.
+// fa_fwd_ex's work; `single` selects the single-buffered race-check variant,
+// `ws` / `ws_bytes` the caller's workspace of fa_fwd_ws (NULL / 0: none).
 int fwd_entry(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H, int64_t H_kv,
               int64_t S_q, int64_t S_k, int64_t D, int causal, int64_t window_left, int64_t window_right,
-              float scale, int dtype, void* stream, bool single) {
+              float scale, int dtype, void* stream, bool single, void* ws = nullptr, int64_t ws_bytes = 0) {
     // ---- argument checks: no HIP call before all of them pass ----------------
     int rc = check_problem(B, H, H_kv, S_q, S_k, D, causal, window_left, window_right, scale);
     if (rc == FA_ERR_SHAPE || rc == FA_ERR_HEAD_DIM) return rc;
@@ -495,6 +538,17 @@ int fwd_entry(const void* q, const void* k, const void* v, void* o, float* lse, 
         overlaps(lse, lse_bytes, q, tensor_bytes) || overlaps(lse, lse_bytes, k, kv_bytes) ||
         overlaps(lse, lse_bytes, v, kv_bytes))
         return FA_ERR_ALIAS;
+    // the workspace, when given, is written: 16-byte aligned, apart from every
+    // tensor of the call
+    if (ws_bytes < 0) return FA_ERR_WORKSPACE;
+    if (!ws) ws_bytes = 0;
+    if (ws_bytes > 0) {
+        if ((uintptr_t)ws & 15) return FA_ERR_ALIGNMENT;
+        if (overlaps(ws, ws_bytes, q, tensor_bytes) || overlaps(ws, ws_bytes, k, kv_bytes) ||
+            overlaps(ws, ws_bytes, v, kv_bytes) || overlaps(ws, ws_bytes, o, tensor_bytes) ||
+            overlaps(ws, ws_bytes, lse, lse_bytes))
+            return FA_ERR_ALIAS;
+    }
 
     // no keys: every row is empty, O = 0 and lse = ln 0 = -inf
     if (S_k == 0) {
@@ -503,7 +557,8 @@ int fwd_entry(const void* q, const void* k, const void* v, void* o, float* lse, 
     }
     // c = scale * log2(e), rounded once to fp32: scores enter exp2 as S*c - m.
     Fwd a{q, k, v, o, lse, (int)S_q, (int)S_k, (int)BH, (int)(H / H_kv), clip_window(window_left, S),
-          clip_window(window_right, S), (float)((double)scale * 1.4426950408889634), (hipStream_t)stream, single};
+          clip_window(window_right, S), (float)((double)scale * 1.4426950408889634), (hipStream_t)stream, single,
+          ws, ws_bytes};
     return causal ? dispatch_d<true>(D, dtype, a) : dispatch_d<false>(D, dtype, a);
 }
 
@@ -514,6 +569,25 @@ extern "C" int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, f
                          int64_t window_right, float scale, int dtype, void* stream) {
     return fwd_entry(q, k, v, o, lse, B, H, H_kv, S_q, S_k, D, causal, window_left, window_right, scale, dtype,
                      stream, false);
+}
+
+extern "C" int64_t fa_fwd_workspace_bytes(int64_t B, int64_t H, int64_t H_kv, int64_t S_q, int64_t S_k, int64_t D,
+                                          int causal, int64_t window_left, int64_t window_right, int dtype) {
+    if (check_problem(B, H, H_kv, S_q, S_k, D, causal, window_left, window_right, 1.0f) != FA_OK) return 0;
+    if (dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16) return 0;
+    if (B == 0 || H == 0 || S_q == 0 || S_k == 0) return 0;
+    const int64_t S = S_q > S_k ? S_q : S_k;
+    if (check_sizes(B, H, S, D) != FA_OK || S * D * 2 > 2147483647) return 0;
+    return split_workspace_bytes(D, causal != 0, clip_window(window_left, S), clip_window(window_right, S), S_q, S_k,
+                                 B * H);
+}
+
+extern "C" int fa_fwd_ws(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+                         int64_t H_kv, int64_t S_q, int64_t S_k, int64_t D, int causal, int64_t window_left,
+                         int64_t window_right, float scale, int dtype, void* workspace, int64_t workspace_bytes,
+                         void* stream) {
+    return fwd_entry(q, k, v, o, lse, B, H, H_kv, S_q, S_k, D, causal, window_left, window_right, scale, dtype,
+                     stream, false, workspace, workspace_bytes);
 }
 
 extern "C" int fa_fwd_single_buffered(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
@@ -542,7 +616,7 @@ extern "C" const char* fa_status_string(int status) {
         case FA_ERR_ALIGNMENT: return "[B,H,S,D] tensors must be 16-byte aligned, lse and delta 4-byte aligned";
         case FA_ERR_WINDOW: return "window bounds must be >= -1 (-1: no limit on that side)";
         case FA_ERR_UNSUPPORTED: return "fa_fwd_single_buffered: only the two-block kernel (D = 32, 64, fp16 / bf16, B*H*ceil(S/256) >= 512, no window) has a single-buffered variant";
-        case FA_ERR_WORKSPACE: return "B * H * S_q exceeds the static workspace of fa_bwd_noalloc (4,194,304 rows)";
+        case FA_ERR_WORKSPACE: return "workspace: fa_bwd_noalloc needs B * H * S_q <= 4,194,304; fa_fwd_ws needs workspace_bytes >= 0";
         default: return "unknown status";
     }
 }

@@ -53,7 +53,8 @@ extern "C" {
 #define FA_ERR_LAUNCH 9         /* the HIP runtime rejected the kernel launch */
 #define FA_ERR_ALIGNMENT 10     /* a [B,H,S,D] tensor not 16-byte aligned, or lse / delta not 4-byte aligned */
 #define FA_ERR_WINDOW 11        /* a window bound is below -1 */
-#define FA_ERR_WORKSPACE 12     /* fa_bwd_noalloc: B * H * S_q exceeds its static workspace */
+#define FA_ERR_WORKSPACE 12     /* fa_bwd_noalloc: B * H * S_q exceeds its static workspace;
+                                   fa_fwd_ws: workspace_bytes < 0 */
 #define FA_ERR_UNSUPPORTED 13   /* fa_fwd_single_buffered: no single-buffered variant for this problem */
 
 /* ---- element types (the dtype argument) --------------------------------- */
@@ -184,6 +185,56 @@ int fa_bwd_ex(const void *q, const void *k, const void *v, const void *o, const 
               int64_t B, int64_t H, int64_t H_kv, int64_t S_q, int64_t S_k, int64_t D,
               int causal, int64_t window_left, int64_t window_right,
               float scale, int dtype, void *stream);
+
+/*
+ * fa_fwd_workspace_bytes, fa_fwd_ws -- fa_fwd_ex with a caller-given device
+ * workspace, which lets the forward split the longest query blocks of a
+ * causal problem over two workgroups each.  Every workgroup of a causal grid
+ * walks the keys of one query block, so the blocks next to the diagonal's far
+ * end are the longest serial chains; when the whole grid is resident on the
+ * GPU at once they, not the total work, set the time.  With the workspace, the
+ * longer half of the blocks of every head run as two key ranges each, and a
+ * second kernel combines the two partial results (O_1, lse_1), (O_2, lse_2) by
+ * the log-sum-exp rule
+ *
+ *     M = max(lse_1, lse_2),  w_i = exp(lse_i - M),
+ *     O = (w_1 O_1 + w_2 O_2) / (w_1 + w_2),  lse = M + ln(w_1 + w_2)
+ *
+ * (the partial results and their merge through the saved lse: "T5 讲解：
+ * FlashAttention forward", section ⑥; "Inside FlashAttention", section 2.4).
+ * The partials stay fp32, and O is rounded to dtype once, after the merge; the
+ * results equal fa_fwd_ex's to within fp32 rounding (the order of the key
+ * sums differs), not bit for bit.
+ *
+ * fa_fwd_workspace_bytes returns the bytes the split needs for a problem (the
+ * arguments as for fa_fwd_ex), or 0 when fa_fwd_ws runs it without a
+ * workspace, exactly as fa_fwd_ex (no split for that problem, or invalid
+ * arguments, which fa_fwd_ws then reports).  Currently: causal, no window,
+ * S_q = S_k, dtype fp16 or bf16, D = 32 or 64, and 512 workgroups of 256 query
+ * rows (B * H * ceil(S / 256) = 512, the grid the GPU holds at once); the
+ * size is (ceil(S / 256) / 2) * B * H * 2 * 256 * (D + 1) * 4 bytes (about
+ * 33 MiB at B * H = 8, S = 16384, D = 64).  No HIP call.
+ *
+ * fa_fwd_ws: every argument as for fa_fwd_ex, plus
+ *   workspace        device memory, 16-byte aligned, apart from every tensor
+ *                    of the call; NULL with workspace_bytes = 0 is allowed.
+ *   workspace_bytes  its size; >= 0 (FA_ERR_WORKSPACE otherwise).  Below
+ *                    fa_fwd_workspace_bytes(...) the call runs without the
+ *                    split, as fa_fwd_ex.
+ * The call writes the workspace (no initial content is read) and leaves
+ * scratch values there; the caller owns it, and two calls in flight at once
+ * must not share one.  Like every entry point it allocates, frees and
+ * synchronises nothing: with the split it enqueues two kernels on `stream`.
+ * Errors: as for fa_fwd_ex, plus FA_ERR_ALIGNMENT for a misaligned workspace
+ * and FA_ERR_ALIAS for a workspace that overlaps a tensor (when
+ * workspace_bytes > 0).
+ */
+int64_t fa_fwd_workspace_bytes(int64_t B, int64_t H, int64_t H_kv, int64_t S_q, int64_t S_k, int64_t D,
+                               int causal, int64_t window_left, int64_t window_right, int dtype);
+int fa_fwd_ws(const void *q, const void *k, const void *v, void *o, float *lse,
+              int64_t B, int64_t H, int64_t H_kv, int64_t S_q, int64_t S_k, int64_t D,
+              int causal, int64_t window_left, int64_t window_right,
+              float scale, int dtype, void *workspace, int64_t workspace_bytes, void *stream);
 
 /*
  * fa_fwd_single_buffered -- race check of the forward's double-buffered K/V

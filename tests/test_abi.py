@@ -309,3 +309,47 @@ def test_single_buffered_unsupported_problems(fa, over):
     st = fa.fa_fwd_single_buffered(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["S"], a["D"],
                                    a["causal"], a["scale"], a["dtype"], a["stream"])
     assert st == fa.FA_ERR_UNSUPPORTED
+
+
+# ---- fa_fwd_workspace_bytes / fa_fwd_ws: the key split of the longest causal blocks
+
+def test_fwd_workspace_bytes_closed_form(fa):
+    """The split's workspace: (ceil(S/256) / 2) blocks per head, two key halves
+    each, 256 rows of D fp32 values plus the lse; only for the problems the
+    split runs on (causal, no window, S_q = S_k, fp16 / bf16, D = 32 or 64,
+    512 workgroups of 256 rows).  A pure size computation: no HIP call."""
+    def ws(B=8, H=1, Hkv=1, Sq=16384, Sk=16384, D=64, causal=1, wl=-1, wr=-1, dtype=1):
+        return fa.fa_fwd_workspace_bytes(B, H, Hkv, Sq, Sk, D, causal, wl, wr, dtype)
+    assert ws() == (64 // 2) * 8 * 2 * 256 * (64 + 1) * 4 == 34_078_720
+    assert ws(D=32, dtype=2) == 32 * 8 * 2 * 256 * 33 * 4
+    assert ws(Sq=16383, Sk=16383) == ws()                       # a ragged last block: same 64 blocks
+    assert ws(B=4, H=2, Hkv=1) == ws()                          # grouped K/V heads: B * H = 8 query heads
+    assert ws(B=2, H=16, Hkv=4, Sq=4096, Sk=4096) == 8 * 32 * 2 * 256 * 65 * 4  # 16 blocks x 32 heads
+    for over in [dict(causal=0), dict(D=128), dict(D=16), dict(dtype=0), dict(wl=1000), dict(wr=0),
+                 dict(Sk=8192), dict(B=16), dict(B=4), dict(D=48), dict(Hkv=3), dict(dtype=7),
+                 dict(B=0), dict(Sq=-1, Sk=-1)]:
+        assert ws(**over) == 0, over
+    # a window bound of max(S_q, S_k) or more is no window
+    assert ws(wl=16384, wr=1 << 40) == ws()
+
+
+def wscall(fa, ws, ws_bytes, **over):
+    a = dict(XARGS, **over)
+    sq, sk = a.get("Sq", a["S"]), a.get("Sk", a["S"])
+    return fa.fa_fwd_ws(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Hkv"], sq, sk, a["D"],
+                        a["causal"], a["wl"], a["wr"], a["scale"], a["dtype"], ws, ws_bytes, a["stream"])
+
+
+def test_fwd_ws_rejects_bad_workspace(fa):
+    """fa_fwd_ws checks its workspace after fa_fwd_ex's checks and before any
+    HIP call: a negative size, a misaligned or an overlapping workspace."""
+    W = 64 * P  # far from the fake tensors at P .. 5P
+    assert wscall(fa, W, -1) == fa.FA_ERR_WORKSPACE
+    assert wscall(fa, W + 4, 1024) == fa.FA_ERR_ALIGNMENT
+    assert wscall(fa, P + 64, 1024) == fa.FA_ERR_ALIAS             # inside q
+    assert wscall(fa, 5 * P - 64, 1024) == fa.FA_ERR_ALIAS         # runs into lse
+    # fa_fwd_ex's own checks come first
+    assert wscall(fa, W, -1, D=48) == fa.FA_ERR_HEAD_DIM
+    assert wscall(fa, W + 4, 1024, q=0) == fa.FA_ERR_NULL_POINTER
+    # an empty problem is a no-op whatever the workspace
+    assert wscall(fa, 0, 0, B=0, q=0, k=0, v=0, o=0, lse=0) == fa.FA_OK

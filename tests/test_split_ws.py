@@ -1,0 +1,163 @@
+"""GPU parity of the forward's key split (fa_fwd_ws with the workspace that
+fa_fwd_workspace_bytes sizes) against the float64 oracle and against
+fa_fwd_ex.
+
+With the workspace, the longer half of every head's causal query blocks runs
+as two workgroups over the two halves of the block's keys; a second kernel
+merges the two partial results (O_i, lse_i) by the log-sum-exp rule ("T5 讲解：
+FlashAttention forward", section ⑥; "Inside FlashAttention", section 2.4).
+Each half keeps its own running maximum, so its softmax weights are rounded to
+the input type against a different reference than fa_fwd_ex's: the results
+agree with fa_fwd_ex to within the weights' rounding, not bit for bit, and both
+meet the oracle's tolerance.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from parity_util import DT, O_ABS_TOL, check_lse, check_o, sample_rows, to_f64
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("no GPU visible", allow_module_level=True)
+
+import exact_tiled_attention_06_amd as fa  # noqa: E402
+
+fa.library()  # fails loudly when libfa.so is missing
+
+DEV = "cuda:0"
+
+
+def fp32(x):
+    return float(torch.tensor(x, dtype=torch.float32))
+
+
+def ws_bytes(B, H, Hkv, S, D, dtype):
+    return fa.fa_fwd_workspace_bytes(B, H, Hkv, S, S, D, 1, -1, -1, fa.DTYPE_CODES[DT[dtype]])
+
+
+def run(q, k, v, scale, ws=None, nbytes=0):
+    """fa_fwd_ws (fa_fwd_ex when ws is None) on device copies; causal, no window."""
+    B, H, S, D = q.shape
+    qd, kd, vd = (x.to(DEV) for x in (q, k, v))
+    o = torch.empty_like(qd)
+    lse = torch.empty((B, H, S), dtype=torch.float32, device=DEV)
+    stream = torch.cuda.current_stream().cuda_stream
+    code = fa.DTYPE_CODES[q.dtype]
+    if ws is None:
+        st = fa.fa_fwd_ex(qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H,
+                          k.shape[1], S, S, D, 1, -1, -1, scale, code, stream)
+    else:
+        st = fa.fa_fwd_ws(qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H,
+                          k.shape[1], S, S, D, 1, -1, -1, scale, code, ws.data_ptr(), nbytes, stream)
+    fa.check(st)
+    torch.cuda.synchronize()
+    return o.cpu(), lse.cpu()
+
+
+def inputs(B, H, Hkv, S, D, dtype, seed):
+    q, _, _ = workloads.make_inputs(B, H, S, D, dtype, seed)
+    _, k, v = workloads.make_inputs(B, Hkv, S, D, dtype, seed + 1)
+    return q, k, v
+
+
+# B * H * ceil(S / 256) = 512: the grid the split runs on
+SPLIT_CASES = [
+    (2, 16, 2, 4096, 64, "f16"),     # 16 blocks per head, 8 split; grouped K/V heads
+    (16, 16, 16, 512, 64, "bf16"),   # 2 blocks per head, the last one split
+    (8, 16, 16, 1000, 64, "f16"),    # ragged last block (232 rows), 2 of 4 split
+    (4, 16, 4, 2048, 32, "bf16"),    # D = 32, grouped K/V heads
+    (8, 8, 8, 2000, 32, "f16"),      # D = 32, ragged
+]
+
+
+def test_split_matches_oracle_and_fa_fwd_ex():
+    """Every element of O and lse against the oracle, for each case in turn on
+    one shared workspace (first filled with NaN, then reused with the previous
+    case's contents: the call must read none of it), and against fa_fwd_ex."""
+    need = max(ws_bytes(B, H, Hkv, S, D, dt) for B, H, Hkv, S, D, dt in SPLIT_CASES)
+    ws = torch.full((need // 4,), float("nan"), dtype=torch.float32, device=DEV)
+    for i, (B, H, Hkv, S, D, dtype) in enumerate(SPLIT_CASES):
+        n_qblk = -(-S // 256)
+        nbytes = ws_bytes(B, H, Hkv, S, D, dtype)
+        assert nbytes == (n_qblk // 2) * B * H * 2 * 256 * (D + 1) * 4
+        q, k, v = inputs(B, H, Hkv, S, D, dtype, 8100 + 7 * i)
+        scale = fp32(1 / math.sqrt(D))
+        what = f"{dtype} B={B} H={H} Hkv={Hkv} S={S} D={D}"
+        print(f"\nsplit case {what}", flush=True)
+        o, lse = run(q, k, v, scale, ws, nbytes)
+        o_ref, l_ref = oracle.attention(to_f64(q), to_f64(k), to_f64(v), True, scale)
+        e = check_o(to_f64(o), o_ref, dtype, f"O {what}")
+        check_lse(to_f64(lse), l_ref, f"lse {what}")
+        o_ex, lse_ex = run(q, k, v, scale)
+        d = float((o.double() - o_ex.double()).abs().max())
+        dl = float((lse.double() - lse_ex.double()).abs().max())
+        print(f"  max|dO| vs oracle {e:.3e}, vs fa_fwd_ex {d:.3e}; max|dlse| vs fa_fwd_ex {dl:.3e}", flush=True)
+        assert d <= O_ABS_TOL[dtype]
+        assert dl <= 1e-4 * max(1.0, float(lse_ex.abs().max()))
+        # causal row 0 sees key 0 alone: O = V[0] exactly (row 0 is in no split block)
+        assert torch.equal(o[:, :, 0], v.repeat_interleave(H // Hkv, dim=1)[:, :, 0])
+
+
+def test_short_workspace_runs_fa_fwd_ex():
+    """A workspace below fa_fwd_workspace_bytes, or none, runs fa_fwd_ex's
+    kernel: the same bits."""
+    B, H, Hkv, S, D, dtype = 16, 16, 16, 512, 64, "f16"
+    q, k, v = inputs(B, H, Hkv, S, D, dtype, 8200)
+    scale = fp32(1 / math.sqrt(D))
+    nbytes = ws_bytes(B, H, Hkv, S, D, dtype)
+    ws = torch.zeros(nbytes // 4, dtype=torch.float32, device=DEV)
+    o_ex, lse_ex = run(q, k, v, scale)
+    for short in (nbytes - 16, 0):
+        o, lse = run(q, k, v, scale, ws, short)
+        assert torch.equal(o, o_ex) and torch.equal(lse, lse_ex), short
+
+
+def test_no_split_problem_ignores_workspace():
+    """Where fa_fwd_workspace_bytes is 0 (here a non-causal problem), a given
+    workspace changes nothing."""
+    B, H, S, D = 8, 16, 1000, 64
+    q, k, v = inputs(B, H, H, S, D, "f16", 8300)
+    scale = fp32(1 / math.sqrt(D))
+    assert fa.fa_fwd_workspace_bytes(B, H, H, S, S, D, 0, -1, -1, fa.FA_DTYPE_F16) == 0
+    ws = torch.zeros(1 << 20, dtype=torch.float32, device=DEV)
+    qd, kd, vd = (x.to(DEV) for x in (q, k, v))
+    outs = []
+    for use_ws in (False, True):
+        o = torch.empty_like(qd)
+        lse = torch.empty((B, H, S), dtype=torch.float32, device=DEV)
+        stream = torch.cuda.current_stream().cuda_stream
+        args = (qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, H, S, S, D, 0,
+                -1, -1, scale, fa.FA_DTYPE_F16)
+        st = (fa.fa_fwd_ws(*args, ws.data_ptr(), ws.numel() * 4, stream) if use_ws
+              else fa.fa_fwd_ex(*args, stream))
+        fa.check(st)
+        torch.cuda.synchronize()
+        outs.append((o.cpu(), lse.cpu()))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
+@pytest.mark.parametrize("name", ["sweep_D64_S16384", "sweep_D32_S16384"])
+def test_full_size_sampled_rows(name):
+    """At the full B=8 H=1 S=16384 size (64 blocks per head, 32 split): the
+    oracle row by row on the first and last rows of every head, rows on both
+    sides of block boundaries (the split blocks' included) and random rows."""
+    w = workloads.BY_NAME[name]
+    q, k, v = workloads.workload_inputs(w)
+    scale = fp32(1 / math.sqrt(w.D))
+    nbytes = ws_bytes(w.B, w.H, w.kv_heads, w.S, w.D, w.dtype)
+    assert nbytes > 0
+    ws = torch.empty(nbytes // 4, dtype=torch.float32, device=DEV)
+    o, lse = run(q, k, v, scale, ws, nbytes)
+    rows = sample_rows(w.B, w.H, w.S, 256, seed=8400)
+    o_ref, l_ref = oracle.attention_rows(to_f64(q), to_f64(k), to_f64(v), True, scale, rows)
+    of = to_f64(o).reshape(-1, w.D)[rows]
+    lf = to_f64(lse).reshape(-1)[rows]
+    check_o(of, np.asarray(o_ref).reshape(of.shape), w.dtype, f"O {name}")
+    check_lse(lf, np.asarray(l_ref).reshape(lf.shape), f"lse {name}")
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
