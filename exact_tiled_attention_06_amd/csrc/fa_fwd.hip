@@ -100,23 +100,40 @@ int fill_words(void* p, uint32_t value, int64_t bytes, hipStream_t stream) {
     return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
-// Workspace for the key split of the longest blocks (fa_fwd_split_kernel with
-// nsplit > 0), 0 when the problem does not use it.  The split pays where the
-// two-block kernel's whole grid is resident at once (at most 2 * kCUs
-// workgroups of 256 rows; it is used from kFullGrid = 2 * kCUs up, so exactly
-// that many): there the longest blocks' serial chains of tiles set the time
-// (per-wave timestamps: the longest block runs 30 % longer than the mean
-// load of a compute unit).  The n_qblk / 2 longest blocks of every head then
-// run as two key halves each, with an fp32 partial of 256 rows x (D + 1)
-// values per half.  Causal, no window, D = 32 or 64 (the two-block kernel),
-// S_q = S_k (every row of a split block then sees keys in both halves).
+// Rows per workgroup of the kernel a causal problem without a window runs on,
+// where that kernel can split its longest blocks' keys (0 elsewhere): the
+// two-block kernel at D = 32, 64 (256 rows, from kFullGrid workgroups), the
+// one-block kernel at D = 16 (128 rows, same rule) and at D = 128 between the
+// key-split kernel and the large tile (128 rows).  Mirrors launch_mfma.
+int64_t split_rows(int64_t D, int64_t S, int64_t BH) {
+    auto grid = [&](int64_t bm) { return (S + bm - 1) / bm * BH; };
+    if (D == 32 || D == 64) return grid(256) >= kFullGrid ? 256 : 0;
+    if (D == 16) return grid(128) >= kFullGrid ? 128 : 0;
+    return (grid(256) < kFullGrid && grid(64) >= kFullGrid) ? 128 : 0;
+}
+
+// Largest grid (workgroups of split_rows rows) whose longest blocks are split:
+// where the whole grid is resident at once.  At D = 128 only a grid of one
+// workgroup per compute unit: at two per unit (B=8 H=1 S=8192) the split
+// measured no gain (156.0 against 156.8 us).
+int64_t split_max_grid(int64_t D) { return D == 128 ? kCUs : 2 * kCUs; }
+
+// Workspace for the key split of the longest blocks (nsplit > 0 in the
+// two-block and one-block kernels), 0 when the problem does not use it.  The
+// split pays where a kernel's whole grid is resident at once (at most
+// 2 * kCUs workgroups, two per compute unit): there no later workgroup
+// balances the load, and the longest blocks' serial chains of tiles set the
+// time.  The n_qblk / 2 longest blocks of every head then run as two key
+// halves each, with an fp32 partial of BM rows x (D + 1) values per half, and
+// the work items start longest first.  Causal, no window, S_q = S_k (every
+// row of a split block then sees keys in both halves).
 int64_t split_workspace_bytes(int64_t D, bool causal, int wl, int wr, int64_t Sq, int64_t Sk, int64_t BH) {
-    constexpr int64_t kBM = 256;  // rows per two-block workgroup (4 waves x 64)
-    if (!causal || wl >= 0 || wr >= 0 || (D != 32 && D != 64) || Sq != Sk) return 0;
-    const int64_t n_qblk = (Sq + kBM - 1) / kBM;
-    const int64_t grid = n_qblk * BH;
-    if (grid < kFullGrid || grid > 2 * kCUs || n_qblk < 2) return 0;
-    return (n_qblk / 2) * BH * 2 * kBM * (D + 1) * 4;
+    if (!causal || wl >= 0 || wr >= 0 || Sq != Sk) return 0;
+    const int64_t bm = split_rows(D, Sq, BH);
+    if (bm == 0) return 0;
+    const int64_t n_qblk = (Sq + bm - 1) / bm;
+    if (n_qblk * BH > split_max_grid(D) || n_qblk < 2) return 0;
+    return (n_qblk / 2) * BH * 2 * bm * (D + 1) * 4;
 }
 
 // The `round` argument of the two-block and key-split kernels.  When two of
@@ -144,35 +161,41 @@ int launch_cfg(const Fwd& a) {
     const int n_qblk = (a.Sq + Cfg::BM - 1) / Cfg::BM;
     const int64_t grid = (int64_t)n_qblk * a.BH;
     if (grid > (int64_t)1 << 24) return FA_ERR_TOO_LARGE;
+    // the key split of the longest blocks, when the caller's workspace holds it
+    int nsplit = 0;
+    float *po = nullptr, *pl = nullptr;
+    if constexpr (!SINGLE && Cfg::CAUSAL) {
+        const int64_t need = split_workspace_bytes(Cfg::D, true, a.wl, a.wr, a.Sq, a.Sk, a.BH);
+        if (need > 0 && a.ws && a.ws_bytes >= need && split_rows(Cfg::D, a.Sq, a.BH) == Cfg::BM) {
+            nsplit = n_qblk / 2;
+            po = (float*)a.ws;
+            pl = po + (int64_t)nsplit * a.BH * 2 * Cfg::BM * Cfg::D;
+        }
+    }
+    const int64_t g = grid + (int64_t)nsplit * a.BH;  // each split block: two workgroups
     (void)hipGetLastError();  // clear a stale error so the check below sees this launch only
-    if constexpr (Cfg::QB == 2 && Cfg::KB == 1 && Cfg::PIPE) {
-        // the key split of the longest blocks, when the caller's workspace holds it
-        int nsplit = 0;
-        float *po = nullptr, *pl = nullptr;
-        if constexpr (!SINGLE) {
-            const int64_t need = split_workspace_bytes(Cfg::D, Cfg::CAUSAL, a.wl, a.wr, a.Sq, a.Sk, a.BH);
-            if (need > 0 && a.ws && a.ws_bytes >= need) {
-                nsplit = n_qblk / 2;
-                po = (float*)a.ws;
-                pl = po + (int64_t)nsplit * a.BH * 2 * Cfg::BM * Cfg::D;
-            }
-        }
-        const int64_t g = grid + (int64_t)nsplit * a.BH;  // each split block: two workgroups
-        hipLaunchKernelGGL((fa_fwd_split_kernel<T, Cfg, SINGLE>), dim3((unsigned)g), dim3(Cfg::NT), 0, a.stream,
-                           (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o,
-                           a.lse, a.Sq, a.Sk, a.BH, n_qblk, a.G, a.c,
-                           nsplit ? 0 : two_round_order<Cfg, 4 * Cfg::TILE, true>(grid), po, pl, nsplit);
-        if (nsplit) {
-            if (hipGetLastError() != hipSuccess) return FA_ERR_LAUNCH;
-            const int64_t threads = (int64_t)nsplit * a.BH * Cfg::BM * (Cfg::D / 4);
-            hipLaunchKernelGGL((fa_fwd_merge_kernel<T, Cfg::D, Cfg::BM>), dim3((unsigned)((threads + 255) / 256)),
-                               dim3(256), 0, a.stream, (const float*)po, (const float*)pl, (uint16_t*)a.o, a.lse,
-                               a.Sq, a.BH, n_qblk, nsplit);
-        }
-    } else {
-        hipLaunchKernelGGL((fa_fwd_mfma_kernel<T, Cfg>), dim3((unsigned)grid), dim3(Cfg::NT), 0, a.stream,
-                           (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o,
-                           a.lse, a.Sq, a.Sk, a.BH, n_qblk, a.G, a.c);
+    // (the split runs its own kernel instances, so that the plain ones carry
+    // none of its code)
+    auto launch = [&](auto ksplit) {
+        constexpr bool KS = decltype(ksplit)::value && !SINGLE && Cfg::CAUSAL;
+        if constexpr (Cfg::QB == 2 && Cfg::KB == 1 && Cfg::PIPE)
+            hipLaunchKernelGGL((fa_fwd_split_kernel<T, Cfg, SINGLE, KS>), dim3((unsigned)g), dim3(Cfg::NT), 0,
+                               a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                               (uint16_t*)a.o, a.lse, a.Sq, a.Sk, a.BH, n_qblk, a.G, a.c,
+                               KS ? 0 : two_round_order<Cfg, 4 * Cfg::TILE, true>(grid), po, pl, nsplit);
+        else
+            hipLaunchKernelGGL((fa_fwd_mfma_kernel<T, Cfg, KS>), dim3((unsigned)g), dim3(Cfg::NT), 0, a.stream,
+                               (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o,
+                               a.lse, a.Sq, a.Sk, a.BH, n_qblk, a.G, a.c, po, pl, nsplit);
+    };
+    if (nsplit) launch(std::true_type{});
+    else launch(std::false_type{});
+    if (nsplit) {
+        if (hipGetLastError() != hipSuccess) return FA_ERR_LAUNCH;
+        const int64_t threads = (int64_t)nsplit * a.BH * Cfg::BM * (Cfg::D / 4);
+        hipLaunchKernelGGL((fa_fwd_merge_kernel<T, Cfg::D, Cfg::BM>), dim3((unsigned)((threads + 255) / 256)),
+                           dim3(256), 0, a.stream, (const float*)po, (const float*)pl, (uint16_t*)a.o, a.lse, a.Sq,
+                           a.BH, n_qblk, nsplit);
     }
     return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }

@@ -217,6 +217,70 @@ __device__ __forceinline__ int causal_work_index(int round, int BH) {
     return lin;
 }
 
+// The work items of one head when its nsplit longest causal blocks are split
+// into two key halves (blocks m = n - nsplit .. n - 1 as two halves, blocks
+// 0 .. m - 1 whole; causal block q holds q + 1 blocks' worth of keys, so in
+// units of half that, half q has length q + 1 and whole q length 2(q + 1)),
+// listed longest first (a whole block before two halves of its length, part 0
+// before part 1).
+// The grid is resident all at once and the hardware starts each further
+// workgroup on the first free slot, so this order is the longest-processing-
+// time-first rule: long items start together and short ones fill the gaps.
+// Item `rank` is found by a binary search on its length L: count(L), the
+// number of items of length >= L, is a closed form.
+__device__ __forceinline__ void split_work_item(int rank, int n, int nsplit, int& qblk, int& part) {
+    const int m = n - nsplit;
+    auto count = [&](int L) {  // items of length >= L (L >= 1)
+        const int halves = 2 * max(0, n - max(m, L - 1));
+        const int wholes = max(0, m - max(0, (L + 1) / 2 - 1));
+        return halves + wholes;
+    };
+    // largest L in [1, 2n] with count(L) > rank (count(1) = n + nsplit > rank)
+    int lo = 1, hi = 2 * n;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) / 2;
+        if (count(mid) > rank) lo = mid;
+        else hi = mid - 1;
+    }
+    int off = rank - count(lo + 1);  // position among the items of length lo
+    const int qw = lo / 2 - 1;       // the whole block of this length, if any
+    if ((lo & 1) == 0 && qw >= 0 && qw < m) {
+        if (off == 0) {
+            qblk = qw;
+            part = -1;
+            return;
+        }
+        --off;
+    }
+    qblk = lo - 1;  // the split block of this length: part 0, then part 1
+    part = off;
+}
+
+// A key half's partial result for one 32-row column block of a wave (fp32,
+// rows `row0` + n of the workspace, n = lane % 32): O normalised by the half's
+// own l, and its lse = ln2 * (m + log2 l) (-inf for a row with no key in the
+// half: weight 0 in the merge).
+template <int D, int DB>
+__device__ __forceinline__ void store_partial(float* __restrict__ PO, float* __restrict__ PL, int64_t row0,
+                                              const f32x16 (&o)[DB], float l_lane, float m, int n, int h) {
+    const float l = halves_sum(l_lane);
+    const float inv = l > 0.f ? 1.0f / l : 0.f;
+    const int64_t row = row0 + n;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int d = db * 32 + 8 * g + 4 * h;
+            if (d < D) {
+                f32x4 w;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) w[e] = o[db][4 * g + e] * inv;
+                *reinterpret_cast<f32x4*>(PO + row * D + d) = w;
+            }
+        }
+    if (h == 0) PL[row] = kLn2 * (m + log2_fast(l));
+}
+
 // Per-wave state and the pieces of work on one tile.
 template <typename T, typename Cfg>
 struct WaveTile {
@@ -441,11 +505,12 @@ struct WaveTile {
     }
 };
 
-template <typename T, typename Cfg>
+template <typename T, typename Cfg, bool KSPLIT = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(Cfg::NT, Cfg::NT), amdgpu_waves_per_eu(Cfg::OCC, Cfg::OCC)))
 void fa_fwd_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                         const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
-                        int Sq, int Sk, int BH, int n_qblk, int G, float c) {
+                        int Sq, int Sk, int BH, int n_qblk, int G, float c, float* __restrict__ PO,
+                        float* __restrict__ PL, int nsplit) {
     using W = WaveTile<T, Cfg>;
     constexpr int D = Cfg::D, QB = Cfg::QB, KB = Cfg::KB, KS = Cfg::KS, DB = Cfg::DB;
     constexpr int BN = Cfg::BN, BM = Cfg::BM, BMW = Cfg::BMW, RB = Cfg::RB;
@@ -468,26 +533,52 @@ void fa_fwd_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
     // Workgroup -> (head, query block).  Heads vary fastest so that the
     // workgroups of one head land on one XCD (dispatch is round-robin over the
     // 8 XCDs) and share its K/V in that XCD's L2; causal blocks go longest first.
-    const int wg = blockIdx.x;
-    const int bh = wg % BH;
-    const int rank = wg / BH;
-    const int qblk = CAUSAL ? (n_qblk - 1 - rank) : rank;
+    // With KSPLIT (causal, a workspace PO / PL) the nsplit longest blocks of
+    // every head run as two workgroups over the two halves of their keys
+    // (split_work_item), each writing an fp32 partial result that
+    // fa_fwd_merge_kernel combines by the log-sum-exp rule ("T5 讲解", section
+    // ⑥; "Inside FlashAttention", section 2.4).
+    int bh, qblk;
+    int part = -1;  // -1: the whole block; 0, 1: its first or second key half
+    if constexpr (KSPLIT) {
+        static_assert(CAUSAL, "the key split serves causal problems");
+        bh = blockIdx.x % BH;
+        split_work_item(blockIdx.x / BH, n_qblk, nsplit, qblk, part);
+    } else {
+        const int wg = blockIdx.x;
+        bh = wg % BH;
+        const int rank = wg / BH;
+        qblk = CAUSAL ? (n_qblk - 1 - rank) : rank;
+    }
     const int q0 = qblk * BM;
     const int qw = q0 + wave * BMW;
 
+    // The block's key tiles and this workgroup's range [tb, te) of them (all,
+    // for a whole block; halves split at a multiple of the LDS tile).  The K/V
+    // resources start at key kb = tb * BN, and tile indices, key limits and
+    // masks below are relative to it (kb = 0 for a whole block).
+    constexpr int SUB = Cfg::TBN / BN;
+    const int ntiles_blk = ((CAUSAL ? min(q0 + BM, Sk) : Sk) + BN - 1) / BN;
+    const int tsplit = (ntiles_blk / 2) / SUB * SUB;
+    const int tb = part == 1 ? tsplit : 0;
+    const int te = part == 0 ? tsplit : ntiles_blk;
+    const int kb = tb * BN;
+    const int Skr = Sk - kb;  // keys from kb on
+    const int qwr = qw - kb;  // this wave's first query, relative to kb
+
     const int64_t head = (int64_t)bh * Sq * D;
-    const int64_t kvhead = (int64_t)(bh / G) * Sk * D;  // grouped heads: G query heads per K/V head
+    // grouped heads: G query heads per K/V head
+    const int64_t kvhead = (int64_t)(bh / G) * Sk * D + (int64_t)kb * D;
     const uint16_t* qh = Q + head;
-    const __amdgpu_buffer_rsrc_t krs = head_rsrc<T>(K + kvhead, Sk * RB);
-    const __amdgpu_buffer_rsrc_t vrs = head_rsrc<T>(V + kvhead, Sk * RB);
+    const __amdgpu_buffer_rsrc_t krs = head_rsrc<T>(K + kvhead, Skr * RB);
+    const __amdgpu_buffer_rsrc_t vrs = head_rsrc<T>(V + kvhead, Skr * RB);
     const uint32_t koff = tile_lane_offset<Cfg, false>(wave, lane);
     const uint32_t voff = tile_lane_offset<Cfg, true>(wave, lane);
 
-    const int kend = CAUSAL ? min(q0 + BM, Sk) : Sk;
-    const int ntiles = (kend + BN - 1) / BN;
+    const int ntiles = te - tb;
     // tiles this wave attends to (its last query's diagonal for causal)
     const int wend = CAUSAL ? min(qw + BMW, Sk) : Sk;
-    const int wtiles = qw < Sq ? min(ntiles, (wend + BN - 1) / BN) : 0;
+    const int wtiles = qw < Sq ? max(0, min(te, (wend + BN - 1) / BN) - tb) : 0;
 
     // First tiles in flight before anything else: K(0) and, pipelined, K(1);
     // otherwise K(0) and V(0).
@@ -505,7 +596,7 @@ void fa_fwd_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         const int qrow = min(qw + qb * 32 + n, Sq - 1);
-        last[qb] = CAUSAL ? min(qrow, Sk - 1) : Sk - 1;
+        last[qb] = (CAUSAL ? min(qrow, Sk - 1) : Sk - 1) - kb;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
             qf[qb][ks] = *reinterpret_cast<const u32x4*>(qh + (int64_t)qrow * D + ks * 16 + h * 8);
@@ -552,7 +643,6 @@ void fa_fwd_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
     if constexpr (!Cfg::PIPE) {
         // One LDS tile (TBN keys) per barrier; inside it, compute steps of BN
         // keys: S, (mask), softmax, P*V -- single register sets.
-        constexpr int SUB = Cfg::TBN / BN;
         const int nlds = (ntiles + SUB - 1) / SUB;
         auto simple = [&](int lt, FA_LDS char* kc, FA_LDS char* vc, FA_LDS char* kn, FA_LDS char* vn)
                           __attribute__((always_inline)) {
@@ -568,7 +658,7 @@ void fa_fwd_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
                 if (t >= wtiles) break;  // wave-uniform
                 const int k0 = t * BN;
                 W::qk(kc + sub * BN * RB, offk, qf, sA);
-                if ((CAUSAL && k0 + BN - 1 > qw) || k0 + BN > Sk) W::mask(sA, last, k0, h);
+                if ((CAUSAL && k0 + BN - 1 > qwr) || k0 + BN > Skr) W::mask(sA, last, k0, h);
                 if (t == 0) {
                     W::first(sA, m_run, l_run, c, pA);
                 } else {
@@ -607,7 +697,7 @@ void fa_fwd_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
             if constexpr (KIND == 0) {
                 if (t >= wtiles) return;
                 if (t + 1 < wtiles) W::qk(kn, offk, qf, s_nxt);
-                if ((CAUSAL && k0 + BN - 1 > qw) || k0 + BN > Sk) W::mask(s_cur, last, k0, h);
+                if ((CAUSAL && k0 + BN - 1 > qwr) || k0 + BN > Skr) W::mask(s_cur, last, k0, h);
                 W::first(s_cur, m_run, l_run, c, p_cur);
                 return;
             }
@@ -623,7 +713,7 @@ void fa_fwd_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
                 }
                 if (do_qk) W::qk(kn, offk, qf, s_nxt);
                 W::pv(vp, offv, p_prv, oacc);
-                if ((CAUSAL && k0 + BN - 1 > qw) || k0 + BN > Sk) W::mask(s_cur, last, k0, h);
+                if ((CAUSAL && k0 + BN - 1 > qwr) || k0 + BN > Skr) W::mask(s_cur, last, k0, h);
                 W::expo(s_cur, m_run, c, p_cur, rs);
             }
             // P*V of tile t-1 is in acc now, so a rescale covers every earlier term.
@@ -636,7 +726,7 @@ void fa_fwd_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
         using Edge = std::integral_constant<int, 2>;
 
         // leading tiles that need no mask for any of this wave's rows
-        const int unmasked = min(CAUSAL ? (qw + 1) / BN : ntiles, Sk / BN);
+        const int unmasked = min(CAUSAL ? (qwr + 1) / BN : ntiles, Skr / BN);
         const int steady_end = min(wtiles - 1, unmasked);  // steady for 1 <= t < steady_end
 
         iter(First{}, 0, kbuf[0], kbuf[1], vbuf[0], vbuf[1], sA, sB, pA, pB);
@@ -659,6 +749,15 @@ void fa_fwd_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
     }
 
     // ---- epilogue: O = acc / l, lse = ln2 * (m + log2 l) ---------------------------
+    if (KSPLIT && part >= 0) {
+        // a key half: its fp32 partial, item (2j + part) * BH + bh of BM rows
+        // (j: the block's rank among the split ones), rows in block order
+        const int64_t item = ((int64_t)(2 * (n_qblk - 1 - qblk) + part) * BH + bh) * BM;
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+            store_partial<D, DB>(PO, PL, item + (qw - q0) + 32 * qb, oacc[qb], l_run[qb], m_run[qb], n, h);
+        return;
+    }
     uint16_t* oh = O + head;
     float* lh = LSE + (int64_t)bh * Sq;
 #pragma unroll
@@ -682,6 +781,41 @@ void fa_fwd_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
             if (h == 0) lh[qrow] = kLn2 * (m_run[qb] + log2_fast(l));
         }
     }
+}
+
+// Combines the two key halves of every split block (fa_fwd_split_kernel with
+// nsplit > 0) by the log-sum-exp rule: with partial results (O_h, lse_h),
+//     M = max_h lse_h,  w_h = exp(lse_h - M),  O = sum_h w_h O_h / sum_h w_h,
+//     lse = M + ln(sum_h w_h),
+// rounded to the input type once.  One thread per 4 dims of a row.
+template <typename T, int D, int BM>
+__global__ __launch_bounds__(256) void fa_fwd_merge_kernel(const float* __restrict__ PO, const float* __restrict__ PL,
+                                                           uint16_t* __restrict__ O, float* __restrict__ LSE, int Sq,
+                                                           int BH, int n_qblk, int nsplit) {
+    constexpr int CH = D / 4;  // 4-dim chunks per row
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (t >= (int64_t)nsplit * BH * BM * CH) return;
+    const int chunk = (int)(t % CH);
+    const int64_t r = t / CH;
+    const int i = (int)(r % BM);
+    const int bh = (int)((r / BM) % BH);
+    const int j = (int)(r / ((int64_t)BM * BH));
+    const int qrow = (n_qblk - 1 - j) * BM + i;
+    if (qrow >= Sq) return;
+    const int64_t r0 = ((int64_t)(2 * j) * BH + bh) * BM + i;
+    const int64_t r1 = ((int64_t)(2 * j + 1) * BH + bh) * BM + i;
+    const float l0 = PL[r0], l1 = PL[r1];
+    const float mx = fmaxf(l0, l1);
+    const float w0 = exp2_fast((l0 - mx) * kLog2e), w1 = exp2_fast((l1 - mx) * kLog2e);
+    const float ws = w0 + w1;
+    const float inv = 1.0f / ws;
+    const f32x4 a = *reinterpret_cast<const f32x4*>(PO + r0 * D + 4 * chunk);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(PO + r1 * D + 4 * chunk);
+    u32x2 w;
+    w[0] = pack2<T>((w0 * a[0] + w1 * b[0]) * inv, (w0 * a[1] + w1 * b[1]) * inv);
+    w[1] = pack2<T>((w0 * a[2] + w1 * b[2]) * inv, (w0 * a[3] + w1 * b[3]) * inv);
+    *reinterpret_cast<u32x2*>(O + ((int64_t)bh * Sq + qrow) * D + 4 * chunk) = w;
+    if (chunk == 0) LSE[(int64_t)bh * Sq + qrow] = mx + kLn2 * log2_fast(ws);
 }
 
 }  // namespace fa

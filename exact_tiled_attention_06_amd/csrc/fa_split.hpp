@@ -170,45 +170,7 @@ struct SplitTile {
 // order are the same, so its O and lse must equal the double-buffered kernel's
 // bit for bit; a difference would expose a read of a buffer still being
 // refilled.
-// The work items of one head when its nsplit longest causal blocks are split
-// into two key halves (blocks m = n - nsplit .. n - 1 as halves of about
-// 4(q + 1) key tiles, blocks 0 .. m - 1 whole, 8(q + 1) tiles; in units of 4
-// tiles: half q has length q + 1, whole q has length 2(q + 1)), listed longest
-// first (a whole block before two halves of its length, part 0 before part 1).
-// The grid is resident all at once and the hardware starts each further
-// workgroup on the first free slot, so this order is the longest-processing-
-// time-first rule: long items start together and short ones fill the gaps.
-// Item `rank` is found by a binary search on its length L: count(L), the
-// number of items of length >= L, is a closed form.
-__device__ __forceinline__ void split_work_item(int rank, int n, int nsplit, int& qblk, int& part) {
-    const int m = n - nsplit;
-    auto count = [&](int L) {  // items of length >= L (L >= 1)
-        const int halves = 2 * max(0, n - max(m, L - 1));
-        const int wholes = max(0, m - max(0, (L + 1) / 2 - 1));
-        return halves + wholes;
-    };
-    // largest L in [1, 2n] with count(L) > rank (count(1) = n + nsplit > rank)
-    int lo = 1, hi = 2 * n;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) / 2;
-        if (count(mid) > rank) lo = mid;
-        else hi = mid - 1;
-    }
-    int off = rank - count(lo + 1);  // position among the items of length lo
-    const int qw = lo / 2 - 1;       // the whole block of this length, if any
-    if ((lo & 1) == 0 && qw >= 0 && qw < m) {
-        if (off == 0) {
-            qblk = qw;
-            part = -1;
-            return;
-        }
-        --off;
-    }
-    qblk = lo - 1;  // the split block of this length: part 0, then part 1
-    part = off;
-}
-
-template <typename T, typename Cfg, bool SINGLE = false>
+template <typename T, typename Cfg, bool SINGLE = false, bool KSPLIT = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(Cfg::NT, Cfg::NT), amdgpu_waves_per_eu(Cfg::OCC, Cfg::OCC)))
 void fa_fwd_split_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                          const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE, int Sq, int Sk,
@@ -244,8 +206,8 @@ void fa_fwd_split_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
     const int h = lane >> 5;
 
     // Workgroup -> (head, query block): heads vary fastest (one head's blocks
-    // share an XCD's L2), causal blocks longest first.  With nsplit > 0 (causal,
-    // a workspace PO / PL): the nsplit longest blocks of every head are split
+    // share an XCD's L2), causal blocks longest first.  With KSPLIT (causal, a
+    // workspace PO / PL): the nsplit longest blocks of every head are split
     // at a key-tile boundary into two halves, each a workgroup of its own, and
     // every head's items run longest first (split_work_item); a half
     // writes its fp32 partial result (O normalised by its own l, and its lse)
@@ -255,7 +217,8 @@ void fa_fwd_split_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
     // whole grid is resident at once.
     int bh, qblk;
     int part = -1;  // -1: the whole block; 0, 1: its first or second key half
-    if (CAUSAL && nsplit > 0) {
+    if constexpr (KSPLIT) {
+        static_assert(CAUSAL && !SINGLE, "the key split serves causal problems");
         bh = blockIdx.x % BH;
         split_work_item(blockIdx.x / BH, n_qblk, nsplit, qblk, part);
     } else {
@@ -467,31 +430,13 @@ void fa_fwd_split_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
     if (wt[1] == ntiles && ntiles > 0) ST::pv(vfr, p[1], oacc[1]);
 
     // ---- epilogue: O = acc / l, lse = ln2 * (m + log2 l) ---------------------------
-    if (part >= 0) {
+    if (KSPLIT && part >= 0) {
         // a key half: its fp32 partial, item (2j + part) * BH + bh of BM rows
         // (j: the block's rank among the split ones), rows in block order
         const int64_t item = ((int64_t)(2 * (n_qblk - 1 - qblk) + part) * BH + bh) * BM;
 #pragma unroll
-        for (int a = 0; a < 2; ++a) {
-            // (a row without a key in this half would have l = 0: O = 0 and
-            // lse = -inf give it weight 0 in the merge)
-            const float l = halves_sum(l_run[a]);
-            const float inv = l > 0.f ? 1.0f / l : 0.f;
-            const int64_t row = item + (qw - q0) + 32 * a + n;
-#pragma unroll
-            for (int db = 0; db < DB; ++db)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int d = db * 32 + 8 * g + 4 * h;
-                    if (d < D) {
-                        f32x4 w;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) w[e] = oacc[a][db][4 * g + e] * inv;
-                        *reinterpret_cast<f32x4*>(PO + row * D + d) = w;
-                    }
-                }
-            if (h == 0) PL[row] = kLn2 * (m_run[a] + log2_fast(l));
-        }
+        for (int a = 0; a < 2; ++a)
+            store_partial<D, DB>(PO, PL, item + (qw - q0) + 32 * a, oacc[a], l_run[a], m_run[a], n, h);
         return;
     }
     uint16_t* oh = O + head;
@@ -517,41 +462,6 @@ void fa_fwd_split_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
             if (h == 0) lh[qrow] = kLn2 * (m_run[a] + log2_fast(l));
         }
     }
-}
-
-// Combines the two key halves of every split block (fa_fwd_split_kernel with
-// nsplit > 0) by the log-sum-exp rule: with partial results (O_h, lse_h),
-//     M = max_h lse_h,  w_h = exp(lse_h - M),  O = sum_h w_h O_h / sum_h w_h,
-//     lse = M + ln(sum_h w_h),
-// rounded to the input type once.  One thread per 4 dims of a row.
-template <typename T, int D, int BM>
-__global__ __launch_bounds__(256) void fa_fwd_merge_kernel(const float* __restrict__ PO, const float* __restrict__ PL,
-                                                           uint16_t* __restrict__ O, float* __restrict__ LSE, int Sq,
-                                                           int BH, int n_qblk, int nsplit) {
-    constexpr int CH = D / 4;  // 4-dim chunks per row
-    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (t >= (int64_t)nsplit * BH * BM * CH) return;
-    const int chunk = (int)(t % CH);
-    const int64_t r = t / CH;
-    const int i = (int)(r % BM);
-    const int bh = (int)((r / BM) % BH);
-    const int j = (int)(r / ((int64_t)BM * BH));
-    const int qrow = (n_qblk - 1 - j) * BM + i;
-    if (qrow >= Sq) return;
-    const int64_t r0 = ((int64_t)(2 * j) * BH + bh) * BM + i;
-    const int64_t r1 = ((int64_t)(2 * j + 1) * BH + bh) * BM + i;
-    const float l0 = PL[r0], l1 = PL[r1];
-    const float mx = fmaxf(l0, l1);
-    const float w0 = exp2_fast((l0 - mx) * kLog2e), w1 = exp2_fast((l1 - mx) * kLog2e);
-    const float ws = w0 + w1;
-    const float inv = 1.0f / ws;
-    const f32x4 a = *reinterpret_cast<const f32x4*>(PO + r0 * D + 4 * chunk);
-    const f32x4 b = *reinterpret_cast<const f32x4*>(PO + r1 * D + 4 * chunk);
-    u32x2 w;
-    w[0] = pack2<T>((w0 * a[0] + w1 * b[0]) * inv, (w0 * a[1] + w1 * b[1]) * inv);
-    w[1] = pack2<T>((w0 * a[2] + w1 * b[2]) * inv, (w0 * a[3] + w1 * b[3]) * inv);
-    *reinterpret_cast<u32x2*>(O + ((int64_t)bh * Sq + qrow) * D + 4 * chunk) = w;
-    if (chunk == 0) LSE[(int64_t)bh * Sq + qrow] = mx + kLn2 * log2_fast(ws);
 }
 
 }  // namespace fa

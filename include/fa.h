@@ -210,10 +210,13 @@ int fa_bwd_ex(const void *q, const void *k, const void *v, const void *o, const 
  * arguments as for fa_fwd_ex), or 0 when fa_fwd_ws runs it without a
  * workspace, exactly as fa_fwd_ex (no split for that problem, or invalid
  * arguments, which fa_fwd_ws then reports).  Currently: causal, no window,
- * S_q = S_k, dtype fp16 or bf16, D = 32 or 64, and 512 workgroups of 256 query
- * rows (B * H * ceil(S / 256) = 512, the grid the GPU holds at once); the
- * size is (ceil(S / 256) / 2) * B * H * 2 * 256 * (D + 1) * 4 bytes (about
- * 33 MiB at B * H = 8, S = 16384, D = 64).  No HIP call.
+ * S_q = S_k, dtype fp16 or bf16, and a grid the GPU holds at once (at most 512
+ * workgroups of BM query rows): D = 32 or 64 with B * H * ceil(S / 256) = 512
+ * (BM = 256); D = 16 with B * H * ceil(S / 128) = 512 (BM = 128); D = 128
+ * with B * H * ceil(S / 64) >= 512 and B * H * ceil(S / 128) <= 256
+ * (BM = 128).  The size is
+ * (ceil(S / BM) / 2) * B * H * 2 * BM * (D + 1) * 4 bytes (about 33 MiB at
+ * B * H = 8, S = 16384, D = 64).  No HIP call.
  *
  * fa_fwd_ws: every argument as for fa_fwd_ex, plus
  *   workspace        device memory, 16-byte aligned, apart from every tensor

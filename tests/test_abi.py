@@ -314,10 +314,11 @@ def test_single_buffered_unsupported_problems(fa, over):
 # ---- fa_fwd_workspace_bytes / fa_fwd_ws: the key split of the longest causal blocks
 
 def test_fwd_workspace_bytes_closed_form(fa):
-    """The split's workspace: (ceil(S/256) / 2) blocks per head, two key halves
-    each, 256 rows of D fp32 values plus the lse; only for the problems the
-    split runs on (causal, no window, S_q = S_k, fp16 / bf16, D = 32 or 64,
-    512 workgroups of 256 rows).  A pure size computation: no HIP call."""
+    """The split's workspace: (ceil(S/BM) / 2) blocks per head, two key halves
+    each, BM rows of D fp32 values plus the lse; only for the problems the
+    split runs on (causal, no window, S_q = S_k, fp16 / bf16, a grid of at
+    most 512 workgroups of BM rows on the two-block kernel, BM = 256, or the
+    one-block kernel, BM = 128).  A pure size computation: no HIP call."""
     def ws(B=8, H=1, Hkv=1, Sq=16384, Sk=16384, D=64, causal=1, wl=-1, wr=-1, dtype=1):
         return fa.fa_fwd_workspace_bytes(B, H, Hkv, Sq, Sk, D, causal, wl, wr, dtype)
     assert ws() == (64 // 2) * 8 * 2 * 256 * (64 + 1) * 4 == 34_078_720
@@ -325,6 +326,14 @@ def test_fwd_workspace_bytes_closed_form(fa):
     assert ws(Sq=16383, Sk=16383) == ws()                       # a ragged last block: same 64 blocks
     assert ws(B=4, H=2, Hkv=1) == ws()                          # grouped K/V heads: B * H = 8 query heads
     assert ws(B=2, H=16, Hkv=4, Sq=4096, Sk=4096) == 8 * 32 * 2 * 256 * 65 * 4  # 16 blocks x 32 heads
+    # the one-block kernel: 128-row workgroups at D = 128 (between the key-split
+    # kernel and the 256-row tile, at most one per CU) and at D = 16 (512)
+    assert ws(D=128, Sq=4096, Sk=4096, dtype=2) == 16 * 8 * 2 * 128 * 129 * 4
+    assert ws(D=128, Sq=8192, Sk=8192) == 0    # 512 workgroups of 128 rows: two per CU, no gain measured
+    assert ws(D=16, Sq=8192, Sk=8192) == 32 * 8 * 2 * 128 * 17 * 4
+    assert ws(D=128, Sq=2048, Sk=2048) == 0    # the key-split kernel (64-row grid below 512)
+    assert ws(D=16, Sq=4096, Sk=4096) == 0     # 256 workgroups: the key-split kernel
+    assert ws(D=128, B=16, Sq=8192, Sk=8192) == 0  # 1024 workgroups of 128 rows: not resident at once
     for over in [dict(causal=0), dict(D=128), dict(D=16), dict(dtype=0), dict(wl=1000), dict(wr=0),
                  dict(Sk=8192), dict(B=16), dict(B=4), dict(D=48), dict(Hkv=3), dict(dtype=7),
                  dict(B=0), dict(Sq=-1, Sk=-1)]:

@@ -66,13 +66,19 @@ def inputs(B, H, Hkv, S, D, dtype, seed):
     return q, k, v
 
 
-# B * H * ceil(S / 256) = 512: the grid the split runs on
+# grids the split runs on: B * H * ceil(S / 256) = 512 at D = 32, 64 (the
+# two-block kernel); B * H * ceil(S / 128) = 512 at D = 16 and 256 at D = 128
+# (the one-block kernel)
 SPLIT_CASES = [
     (2, 16, 2, 4096, 64, "f16"),     # 16 blocks per head, 8 split; grouped K/V heads
     (16, 16, 16, 512, 64, "bf16"),   # 2 blocks per head, the last one split
     (8, 16, 16, 1000, 64, "f16"),    # ragged last block (232 rows), 2 of 4 split
     (4, 16, 4, 2048, 32, "bf16"),    # D = 32, grouped K/V heads
     (8, 8, 8, 2000, 32, "f16"),      # D = 32, ragged
+    (2, 4, 4, 4096, 128, "bf16"),    # D = 128: 32 blocks of 128 rows per head, 16 split
+    (1, 16, 4, 2000, 128, "f16"),    # D = 128, ragged (80-row last block), grouped K/V heads
+    (16, 8, 8, 512, 16, "f16"),      # D = 16: 4 blocks of 128 rows per head, 2 split
+    (8, 8, 2, 1000, 16, "bf16"),     # D = 16, ragged, grouped K/V heads
 ]
 
 
@@ -83,9 +89,10 @@ def test_split_matches_oracle_and_fa_fwd_ex():
     need = max(ws_bytes(B, H, Hkv, S, D, dt) for B, H, Hkv, S, D, dt in SPLIT_CASES)
     ws = torch.full((need // 4,), float("nan"), dtype=torch.float32, device=DEV)
     for i, (B, H, Hkv, S, D, dtype) in enumerate(SPLIT_CASES):
-        n_qblk = -(-S // 256)
+        bm = 256 if D in (32, 64) else 128
+        n_qblk = -(-S // bm)
         nbytes = ws_bytes(B, H, Hkv, S, D, dtype)
-        assert nbytes == (n_qblk // 2) * B * H * 2 * 256 * (D + 1) * 4
+        assert nbytes == (n_qblk // 2) * B * H * 2 * bm * (D + 1) * 4
         q, k, v = inputs(B, H, Hkv, S, D, dtype, 8100 + 7 * i)
         scale = fp32(1 / math.sqrt(D))
         what = f"{dtype} B={B} H={H} Hkv={Hkv} S={S} D={D}"
@@ -142,11 +149,12 @@ def test_no_split_problem_ignores_workspace():
     assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
 
 
-@pytest.mark.parametrize("name", ["sweep_D64_S16384", "sweep_D32_S16384"])
+@pytest.mark.parametrize("name", ["sweep_D64_S16384", "sweep_D32_S16384", "sweep_D128_S4096",
+                                  "sweep_D16_S8192"])
 def test_full_size_sampled_rows(name):
-    """At the full B=8 H=1 S=16384 size (64 blocks per head, 32 split): the
-    oracle row by row on the first and last rows of every head, rows on both
-    sides of block boundaries (the split blocks' included) and random rows."""
+    """At the full B=8 H=1 size of the sweep points that split: the oracle row
+    by row on the first and last rows of every head, rows on both sides of
+    block boundaries (the split blocks' included) and random rows."""
     w = workloads.BY_NAME[name]
     q, k, v = workloads.workload_inputs(w)
     scale = fp32(1 / math.sqrt(w.D))
