@@ -39,6 +39,7 @@ from __future__ import annotations
 import ctypes
 import math
 import os
+import struct
 
 import torch  # loads the HIP runtime that libfa.so binds to (same soname)
 
@@ -197,6 +198,16 @@ def fa_bwd_noalloc(q: int, k: int, v: int, o: int, dout: int, lse: int, dq: int,
                                         int(window_left), int(window_right), float(scale), int(dtype), stream))
 
 
+def _fp32(x: float) -> float:
+    """x rounded to the nearest float32 (the C ABI's scale argument), without
+    a tensor round trip on every call."""
+    x = float(x)
+    try:
+        return struct.unpack("f", struct.pack("f", x))[0]
+    except OverflowError:  # beyond float32: the library rejects the non-finite scale
+        return math.copysign(math.inf, x)
+
+
 def _window(window):
     if window is None:
         return -1, -1
@@ -243,7 +254,7 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = Fa
     S_k = k.shape[2]
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    scale = float(torch.tensor(scale, dtype=torch.float32))
+    scale = _fp32(scale)
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
@@ -291,7 +302,7 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
         raise ValueError("lse must be a float32 tensor of shape [B,H,S]")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    scale = float(torch.tensor(scale, dtype=torch.float32))
+    scale = _fp32(scale)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(k)
     delta = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
     stream = torch.cuda.current_stream(q.device).cuda_stream
