@@ -44,10 +44,10 @@ struct Tiles {
     static constexpr int BN = (D == 16) ? 64 : 32;
     static constexpr bool PIPE = true;
     // keys per LDS tile (one barrier each): the two-column-block kernel stages
-    // 128 keys at D = 32; at D = 64 its registers leave no room for the longer
-    // unrolled steady loop, which spills, so it stages one 32-key tile; the
-    // pipelined loop stages one compute step per LDS tile
-    static constexpr int TBN = D == 32 ? FA_SPLIT_TBN : BN;
+    // 128 keys at D = 32 and 64 at D = 64 (B=4 H=16 S=4096: 1 % faster than
+    // one 32-key tile per barrier, 128 keys gain less); the pipelined loop
+    // stages one compute step per LDS tile
+    static constexpr int TBN = D == 32 ? FA_SPLIT_TBN : D == 64 ? 64 : BN;
     // smaller grids: 64 query rows per workgroup, 128 at D = 128 (four waves:
     // their transfer offsets repeat per wave, so the pipelined loop fits in
     // 256 VGPRs; with two waves it spilled)

@@ -354,63 +354,70 @@ void fa_fwd_split_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
     // into the other buffers (their last fragments were read before the
     // barrier).  The fragment reads come before the new transfers, so that the
     // compiler, which tracks the transfers' LDS targets, never makes them wait
-    // for a transfer in flight; `kc`, `vc` are the buffers of parity j % 2.
-    auto sync_with = [&](int t, FA_LDS char* kc, FA_LDS char* vc, FA_LDS char* kn, FA_LDS char* vn)
+    // for a transfer in flight; `kc`, `vc` are the buffers of parity j % 2.  The
+    // slot u is a compile-time constant (its offset folds into the reads'
+    // immediate offsets: no per-lane address arithmetic).
+    auto sync_with = [&](int j, auto ucst, FA_LDS char* kc, FA_LDS char* vc, FA_LDS char* kn, FA_LDS char* vn)
                          __attribute__((always_inline)) {
-        const int j = t / SUB, u = t - j * SUB;
-        if (u == 0) {
+        constexpr int U = decltype(ucst)::value;
+        if constexpr (U == 0) {
             wait_vmcnt0();
             __syncthreads();
         }
         // (fenced, so that the scheduler cannot hoist later tiles' fragment
         // reads into earlier half-steps and run out of registers)
         __builtin_amdgcn_sched_barrier(0);
-        ST::read_k(kc + u * BN * RB, offk, kfr);
-        ST::read_v(vc + u * BN * RB, offv, vfr);
+        ST::read_k(kc + U * BN * RB, offk, kfr);
+        ST::read_v(vc + U * BN * RB, offv, vfr);
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (SINGLE) {
             // one buffer: refill it only once every wave has read its last slot
-            if (u == SUB - 1) {
+            if constexpr (U == SUB - 1) {
                 __syncthreads();
                 if (j + 1 < nlds) {
                     load_tile<T, Cfg, false>(kn, krs, koff, (j + 1) * Cfg::TBN + BN, wave, lane);
                     load_tile<T, Cfg, true>(vn, vrs, voff, (j + 1) * Cfg::TBN, wave, lane);
                 }
             }
-        } else if (u == 0 && j + 1 < nlds) {
-            load_tile<T, Cfg, false>(kn, krs, koff, (j + 1) * Cfg::TBN + BN, wave, lane);
-            load_tile<T, Cfg, true>(vn, vrs, voff, (j + 1) * Cfg::TBN, wave, lane);
+        } else if constexpr (U == 0) {
+            if (j + 1 < nlds) {
+                load_tile<T, Cfg, false>(kn, krs, koff, (j + 1) * Cfg::TBN + BN, wave, lane);
+                load_tile<T, Cfg, true>(vn, vrs, voff, (j + 1) * Cfg::TBN, wave, lane);
+            }
         }
     };
     // buffers known at compile time (steady tiles) ...
-    auto sync = [&](auto par, int t) __attribute__((always_inline)) {
+    auto sync = [&](auto par, int j, auto ucst) __attribute__((always_inline)) {
         constexpr int P = decltype(par)::value;
-        sync_with(t, kbuf[P], vbuf[P], kbuf[1 - P], vbuf[1 - P]);
+        sync_with(j, ucst, kbuf[P], vbuf[P], kbuf[1 - P], vbuf[1 - P]);
     };
     // ... or chosen at run time (generic tiles: fewer code copies)
-    auto sync_rt = [&](int t) __attribute__((always_inline)) {
-        const bool odd = (t / SUB) & 1;
-        sync_with(t, odd ? kbuf[1] : kbuf[0], odd ? vbuf[1] : vbuf[0], odd ? kbuf[0] : kbuf[1],
+    auto sync_rt = [&](int j, auto ucst) __attribute__((always_inline)) {
+        const bool odd = j & 1;
+        sync_with(j, ucst, odd ? kbuf[1] : kbuf[0], odd ? vbuf[1] : vbuf[0], odd ? kbuf[0] : kbuf[1],
                   odd ? vbuf[0] : vbuf[1]);
     };
     // steady for 1 <= t < t_steady: both blocks unmasked, every MFMA present
     const int t_steady = min(min(um[0], um[1]), min(wt[1], wt[0] - 1));
     // The SUB compute tiles of LDS tile j (buffers of parity P), all steady ...
     auto lds_steady = [&](auto par, int j) __attribute__((always_inline)) {
-#pragma unroll
-        for (int u = 0; u < SUB; ++u) {
+        static_for<SUB>([&](auto ucst) __attribute__((always_inline)) {
             steady_half(A0{});
-            sync(par, j * SUB + u);
+            sync(par, j, ucst);
             steady_half(A1{});
-        }
+        });
     };
     // ... or under the generic conditions.
     auto lds_generic = [&](int j) __attribute__((always_inline)) {
-        for (int u = 0; u < SUB && j * SUB + u < ntiles; ++u) {
-            half_any(A0{}, j * SUB + u);
-            sync_rt(j * SUB + u);
-            half_any(A1{}, j * SUB + u);
-        }
+        static_for<SUB>([&](auto ucst) __attribute__((always_inline)) {
+            constexpr int U = decltype(ucst)::value;
+            const int t = j * SUB + U;
+            if (t < ntiles) {
+                half_any(A0{}, t);
+                sync_rt(j, ucst);
+                half_any(A1{}, t);
+            }
+        });
     };
     using P0 = std::integral_constant<int, 0>;
     using P1 = std::integral_constant<int, 1>;
