@@ -121,9 +121,8 @@ int64_t split_max_grid(int64_t D) { return D == 128 ? kCUs : 2 * kCUs; }
 // Workspace for the key split of the longest blocks (nsplit > 0 in the
 // two-block and one-block kernels), 0 when the problem does not use it.  The
 // split pays where a kernel's whole grid is resident at once (at most
-// 2 * kCUs workgroups, two per compute unit): there no later workgroup
-// balances the load, and the longest blocks' serial chains of tiles set the
-// time.  The n_qblk / 2 longest blocks of every head then run as two key
+// split_max_grid workgroups): there no later workgroup balances the load, and
+// the longest blocks' serial chains of tiles set the time.  The n_qblk / 2 longest blocks of every head then run as two key
 // halves each, with an fp32 partial of BM rows x (D + 1) values per half, and
 // the work items start longest first.  Causal, no window, S_q = S_k (every
 // row of a split block then sees keys in both halves).
@@ -636,7 +635,7 @@ extern "C" const char* fa_status_string(int status) {
         case FA_ERR_ALIAS: return "outputs must not overlap each other or the inputs";
         case FA_ERR_TOO_LARGE: return "problem size exceeds the kernels' index ranges";
         case FA_ERR_LAUNCH: return "the HIP runtime rejected the kernel launch";
-        case FA_ERR_ALIGNMENT: return "[B,H,S,D] tensors must be 16-byte aligned, lse and delta 4-byte aligned";
+        case FA_ERR_ALIGNMENT: return "[B,H,S,D] tensors and the fa_fwd_ws workspace must be 16-byte aligned, lse and delta 4-byte aligned";
         case FA_ERR_WINDOW: return "window bounds must be >= -1 (-1: no limit on that side)";
         case FA_ERR_UNSUPPORTED: return "fa_fwd_single_buffered: only the two-block kernel (D = 32, 64, fp16 / bf16, B*H*ceil(S/256) >= 512, no window) has a single-buffered variant";
         case FA_ERR_WORKSPACE: return "workspace: fa_bwd_noalloc needs B * H * S_q <= 4,194,304; fa_fwd_ws needs workspace_bytes >= 0";

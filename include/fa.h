@@ -51,7 +51,8 @@ extern "C" {
 #define FA_ERR_TOO_LARGE 8      /* sizes overflow the kernels' index ranges (for fp16 / bf16
                                    also: one head's K or V, S * D * 2 bytes, must be < 2^31) */
 #define FA_ERR_LAUNCH 9         /* the HIP runtime rejected the kernel launch */
-#define FA_ERR_ALIGNMENT 10     /* a [B,H,S,D] tensor not 16-byte aligned, or lse / delta not 4-byte aligned */
+#define FA_ERR_ALIGNMENT 10     /* a [B,H,S,D] tensor or the fa_fwd_ws workspace not 16-byte aligned,
+                                   or lse / delta not 4-byte aligned */
 #define FA_ERR_WINDOW 11        /* a window bound is below -1 */
 #define FA_ERR_WORKSPACE 12     /* fa_bwd_noalloc: B * H * S_q exceeds its static workspace;
                                    fa_fwd_ws: workspace_bytes < 0 */
