@@ -114,11 +114,14 @@ void fa_fwd_ksplit_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
         const int qrow = min(q0 + qb * 32 + n, Sq - 1);
         last[qb] = CAUSAL ? min(qrow, Sk - 1) : Sk - 1;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
+        for (int ks = 0; ks < KS; ++ks)
             qf[qb][ks] = *reinterpret_cast<const u32x4*>(qh + (int64_t)qrow * D + ks * 16 + h * 8);
-            pin(qf[qb][ks]);
-        }
     }
+    // (pinned once every load is in flight, so that their round trips overlap)
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) pin(qf[qb][ks]);
 
     int offk[KS];
 #pragma unroll

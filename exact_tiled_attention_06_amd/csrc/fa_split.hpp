@@ -276,16 +276,20 @@ void fa_fwd_split_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
     load_tile<T, Cfg, true>(vbuf[0], vrs, voff, 0, wave, lane);
 
     // Q^T operand fragments, resident for the whole loop ("T5 讲解", section ③).
+    // Every load is issued before the first pin: a pin right after its load
+    // makes the wave wait out each load's round trip in turn.
     u32x4 qf[2][KS];
 #pragma unroll
     for (int a = 0; a < 2; ++a) {
         const int qrow = min(qw + 32 * a + n, Sq - 1);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
+        for (int ks = 0; ks < KS; ++ks)
             qf[a][ks] = *reinterpret_cast<const u32x4*>(qh + (int64_t)qrow * D + ks * 16 + h * 8);
-            pin(qf[a][ks]);
-        }
     }
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) pin(qf[a][ks]);
 
     int offk[KS];
 #pragma unroll

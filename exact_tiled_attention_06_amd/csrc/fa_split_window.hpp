@@ -102,11 +102,14 @@ void fa_fwd_split_window_kernel(const uint16_t* __restrict__ Q, const uint16_t* 
     for (int a = 0; a < 2; ++a) {
         const int qrow = min(qw + 32 * a + n, Sq - 1);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
+        for (int ks = 0; ks < KS; ++ks)
             qf[a][ks] = *reinterpret_cast<const u32x4*>(Q + head + (int64_t)qrow * D + ks * 16 + h * 8);
-            pin(qf[a][ks]);
-        }
     }
+    // (pinned once every load is in flight, so that their round trips overlap)
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) pin(qf[a][ks]);
 
     int offk[KS];
 #pragma unroll

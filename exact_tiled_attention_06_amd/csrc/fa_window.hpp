@@ -78,10 +78,11 @@ void fa_fwd_window_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
 
     u32x4 qf[1][KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
+    for (int ks = 0; ks < KS; ++ks)
         qf[0][ks] = *reinterpret_cast<const u32x4*>(Q + head + (int64_t)qrow * D + ks * 16 + h * 8);
-        pin(qf[0][ks]);
-    }
+    // (pinned once every load is in flight, so that their round trips overlap)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) pin(qf[0][ks]);
     int offk[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) offk[ks] = n * RB + (((2 * ks + h) ^ swz_k<D>(n)) * 16);
