@@ -47,17 +47,20 @@ struct WaveLoader {
     }
 };
 
-// LDS of one workgroup: per wave two K and two V tiles.  After the loop the
-// same memory holds the exchange of waves 1..NW-1: per lane QB*DB*16
-// accumulators, QB m, QB l.
+// LDS of one workgroup: four arrays (K and V, two buffers each) that hold one
+// tile per wave, declared apart so that the compiler's tracking of the
+// LDS-direct transfers sees which array each one writes (a fragment read then
+// waits only for transfers into its own array).  After the loop the first
+// three arrays hold the accumulators of waves 1..3 (QB*DB*16 per lane) and a
+// small array their m and l.
 template <typename Cfg>
-constexpr int ksplit_xch_bytes() {
-    return (Cfg::QB * Cfg::DB * 16 + 2 * Cfg::QB) * 64 * 4;  // per wave
+constexpr int ksplit_arr_bytes() {
+    return Cfg::NW * Cfg::TILE > Cfg::QB * Cfg::DB * 16 * 64 * 4 ? Cfg::NW * Cfg::TILE
+                                                                  : Cfg::QB * Cfg::DB * 16 * 64 * 4;
 }
 template <typename Cfg>
 constexpr int ksplit_lds_bytes() {
-    return Cfg::NW * 4 * Cfg::TILE > (Cfg::NW - 1) * ksplit_xch_bytes<Cfg>() ? Cfg::NW * 4 * Cfg::TILE
-                                                                               : (Cfg::NW - 1) * ksplit_xch_bytes<Cfg>();
+    return 4 * ksplit_arr_bytes<Cfg>() + (Cfg::NW - 1) * 2 * Cfg::QB * 64 * 4;
 }
 
 template <typename T, typename Cfg>
@@ -72,16 +75,21 @@ void fa_fwd_ksplit_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     constexpr bool CAUSAL = Cfg::CAUSAL;
     static_assert(Cfg::PIPE && Cfg::TBN == BN, "pipelined loop, one compute tile per LDS tile");
 
-    __shared__ __attribute__((aligned(1024))) char lds[ksplit_lds_bytes<Cfg>()];
+    static_assert(NW == 4, "the exchange uses three of the four arrays");
+    constexpr int ARR = ksplit_arr_bytes<Cfg>();
+    __shared__ __attribute__((aligned(1024))) char lk0[ARR];
+    __shared__ __attribute__((aligned(1024))) char lk1[ARR];
+    __shared__ __attribute__((aligned(1024))) char lv0[ARR];
+    __shared__ __attribute__((aligned(1024))) char lv1[ARR];
+    __shared__ __attribute__((aligned(16))) float xml[(NW - 1) * 2 * QB * 64];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 31;
     const int h = lane >> 5;
-    FA_LDS char* const mine = (FA_LDS char*)lds + wave * 4 * TILE;
-    FA_LDS char* const kbuf[2] = {mine, mine + TILE};
-    FA_LDS char* const vbuf[2] = {mine + 2 * TILE, mine + 3 * TILE};
+    FA_LDS char* const kbuf[2] = {(FA_LDS char*)lk0 + wave * TILE, (FA_LDS char*)lk1 + wave * TILE};
+    FA_LDS char* const vbuf[2] = {(FA_LDS char*)lv0 + wave * TILE, (FA_LDS char*)lv1 + wave * TILE};
 
     // Workgroup -> (head, query block): heads vary fastest, causal blocks
     // longest first.  Every wave holds the block's BMW rows.
@@ -330,9 +338,13 @@ void fa_fwd_ksplit_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
 
     // ---- merge the waves' partial results, then the epilogue ------------------------
     __syncthreads();  // every wave is done with its K/V buffers
-    float* const xch = (float*)lds;
-    auto slot = [&](int w, int k) __attribute__((always_inline)) -> float& {
-        return xch[((w - 1) * (QB * DB * 16 + 2 * QB) + k) * 64 + lane];
+    // wave w's accumulators in array w - 1, its m and l in xml
+    auto acc_slot = [&](int w, int k) __attribute__((always_inline)) -> float& {
+        float* const a = (float*)(w == 1 ? lk0 : w == 2 ? lk1 : lv0);
+        return a[k * 64 + lane];
+    };
+    auto ml_slot = [&](int w, int k) __attribute__((always_inline)) -> float& {
+        return xml[((w - 1) * 2 * QB + k) * 64 + lane];
     };
     if (wave > 0) {
 #pragma unroll
@@ -340,9 +352,9 @@ void fa_fwd_ksplit_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
 #pragma unroll
             for (int db = 0; db < DB; ++db)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) slot(wave, (qb * DB + db) * 16 + r) = oacc[qb][db][r];
-            slot(wave, QB * DB * 16 + qb) = m_run[qb];
-            slot(wave, QB * DB * 16 + QB + qb) = l_run[qb];
+                for (int r = 0; r < 16; ++r) acc_slot(wave, (qb * DB + db) * 16 + r) = oacc[qb][db][r];
+            ml_slot(wave, qb) = m_run[qb];
+            ml_slot(wave, QB + qb) = l_run[qb];
         }
     }
     __syncthreads();
@@ -354,7 +366,7 @@ void fa_fwd_ksplit_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
         float mx = mw[0];
 #pragma unroll
         for (int w = 1; w < NW; ++w) {
-            mw[w] = slot(w, QB * DB * 16 + qb);
+            mw[w] = ml_slot(w, qb);
             mx = fmaxf(mx, mw[w]);
         }
         const float a0 = exp2_fast(mw[0] - mx);
@@ -366,11 +378,11 @@ void fa_fwd_ksplit_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
 #pragma unroll
         for (int w = 1; w < NW; ++w) {
             const float aw = exp2_fast(mw[w] - mx);
-            l += aw * slot(w, QB * DB * 16 + QB + qb);
+            l += aw * ml_slot(w, QB + qb);
 #pragma unroll
             for (int db = 0; db < DB; ++db)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) oacc[qb][db][r] += aw * slot(w, (qb * DB + db) * 16 + r);
+                for (int r = 0; r < 16; ++r) oacc[qb][db][r] += aw * acc_slot(w, (qb * DB + db) * 16 + r);
         }
         m_run[qb] = mx;
         l_run[qb] = l;
