@@ -21,7 +21,7 @@ Prints one JSON line.  Also reported:
                 null (--traffic-bytes overrides);
   cpu_baseline  the float64 CPU oracle timed on this host's cores over the
                 whole workload (every row of every head), in the same unit;
-  backward      fa_bwd (dQ, dK, dV) on the same workload with a seeded dO:
+  backward      fa_bwd_ex (dQ, dK, dV) on the same workload with a seeded dO:
                 TFLOP/s with the usual 2.5x-forward FLOP count, HIP-event
                 kernel time, and the oracle's gradients over one head as its
                 CPU baseline (--no-backward skips it).
@@ -163,20 +163,28 @@ def time_graph(fa, torch, w, causal, launches=20, reps=10):
 
 
 def time_backward(fa, torch, w, causal, steps, warmup):
-    """HIP-event times of fa_bwd (dQ kernel, then dK/dV kernel) on the workload,
+    """HIP-event times of fa_bwd_ex (dQ kernel, then dK/dV kernel) on the workload,
     with the forward's O and lse and a seeded dO, outputs preallocated."""
     import workloads
     q, k, v = (x.to("cuda:0") for x in workloads.workload_inputs(w))
     dout = workloads.make_grad(w.B, w.H, w.S, w.D, w.dtype, w.seed + 1000).to("cuda:0")
-    o, lse = fa.forward(q, k, v, causal=causal, scale=w.scale)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
-    delta = torch.empty((w.B, w.H, w.S), dtype=torch.float32, device="cuda:0")
+    window = None if w.window == (-1, -1) else w.window
+    o, lse = fa.forward(q, k, v, causal=causal, scale=w.scale, window=window)
+    # grouped heads: dK and dV are shaped like k, and the C call takes the
+    # K/V head count from k (fa_bwd would take it to be H)
+    B, H, S, D = q.shape
+    hkv, sk = k.shape[1], k.shape[2]
+    if k.shape != (B, hkv, sk, D) or v.shape != k.shape or H % hkv or o.shape != q.shape:
+        raise ValueError(f"backward timing: inconsistent shapes {tuple(q.shape)}, {tuple(k.shape)}")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    delta = torch.empty((B, H, S), dtype=torch.float32, device="cuda:0")
     stream = torch.cuda.current_stream()
     ptrs = [t.data_ptr() for t in (q, k, v, o, dout, lse, dq, dk, dv, delta)]
     code = fa.DTYPE_CODES[q.dtype]
+    wl, wr = w.window
 
     def call():
-        return fa.fa_bwd(*ptrs, w.B, w.H, w.S, w.D, int(causal), w.scale, code, stream.cuda_stream)
+        return fa.fa_bwd_ex(*ptrs, B, H, hkv, S, sk, D, int(causal), wl, wr, w.scale, code, stream.cuda_stream)
 
     fa.check(call())
     for _ in range(warmup):
@@ -202,7 +210,7 @@ def cpu_baseline_backward(w, causal):
     q, k, v = (x[:1, :1].double().numpy() for x in workloads.workload_inputs(w))
     dout = workloads.make_grad(w.B, w.H, w.S, w.D, w.dtype, w.seed + 1000)[:1, :1].double().numpy()
     t0 = time.perf_counter()
-    orc.attention_bwd(q, k, v, dout, causal, w.scale)
+    orc.attention_bwd(q, k, v, dout, causal, w.scale, None if w.window == (-1, -1) else w.window)
     dt = time.perf_counter() - t0
     head_flops = 2.5 * w.flops(causal) / (w.B * w.H)
     return {

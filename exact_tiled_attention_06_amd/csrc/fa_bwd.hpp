@@ -246,11 +246,13 @@ void fa_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict
     // Every fragment load is issued before the first tile's staging, and the
     // values are waited for after it, so the two overlap.
     u32x4 qf[QB][KS], df[QB][KS], of[QB][KS];
+    float lsev[QB];  // the rows' lse, loaded with the fragments
 #pragma unroll
     for (int a = 0; a < QB; ++a) {
         row_frags<KS>(Q + head, qrow[a], D, h, qf[a]);
         row_frags<KS>(dO + head, qrow[a], D, h, df[a]);
         row_frags<KS>(O + head, qrow[a], D, h, of[a]);
+        lsev[a] = LSE[(int64_t)bh * Sq + qrow[a]];
     }
     issue_order();
     // a block with no key tile (a window that leaves its rows no key, S_k < S_q)
@@ -268,7 +270,7 @@ void fa_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict
         if (grp == 0 && h == 0 && qw + 32 * a + n < Sq) DELTA[(int64_t)bh * Sq + qw + 32 * a + n] = delta[a];
         // a row with no key (lse = -inf; all its scores are masked to -inf)
         // takes +inf, so that its masked scores give exp2(-inf) = 0
-        lse2[a] = first[a] <= last[a] ? LSE[(int64_t)bh * Sq + qrow[a]] * kLog2e : __builtin_inff();
+        lse2[a] = first[a] <= last[a] ? lsev[a] * kLog2e : __builtin_inff();
     }
 
     int offk[KS], offv[DB];
