@@ -162,9 +162,10 @@ def time_graph(fa, torch, w, causal, launches=20, reps=10):
     return start.elapsed_time(end) / (launches * reps)
 
 
-def time_backward(fa, torch, w, causal, steps, warmup):
-    """HIP-event times of fa_bwd_ex (dQ kernel, then dK/dV kernel) on the workload,
-    with the forward's O and lse and a seeded dO, outputs preallocated."""
+def backward_call(fa, torch, w, causal):
+    """The fa_bwd_ex call the backward timing makes on the workload (the
+    forward's O and lse, a seeded dO, outputs preallocated): returns
+    (call, (dq, dk, dv))."""
     import workloads
     q, k, v = (x.to("cuda:0") for x in workloads.workload_inputs(w))
     dout = workloads.make_grad(w.B, w.H, w.S, w.D, w.dtype, w.seed + 1000).to("cuda:0")
@@ -183,9 +184,20 @@ def time_backward(fa, torch, w, causal, steps, warmup):
     code = fa.DTYPE_CODES[q.dtype]
     wl, wr = w.window
 
-    def call():
+    # the call holds every buffer it passes by address, so none is freed while
+    # the call can still run
+    buffers = (q, k, v, o, dout, lse, dq, dk, dv, delta)
+
+    def call(_buffers=buffers):
         return fa.fa_bwd_ex(*ptrs, B, H, hkv, S, sk, D, int(causal), wl, wr, w.scale, code, stream.cuda_stream)
 
+    return call, (dq, dk, dv)
+
+
+def time_backward(fa, torch, w, causal, steps, warmup):
+    """HIP-event times of fa_bwd_ex (dQ kernel, then dK/dV kernel) on the workload."""
+    call, _ = backward_call(fa, torch, w, causal)
+    stream = torch.cuda.current_stream()
     fa.check(call())
     for _ in range(warmup):
         call()
