@@ -12,8 +12,10 @@ Prints one JSON line.  Also reported:
                 SQ_ACTIVE_INST_VALU against the kernel's SIMD-cycles, from the
                 committed rocprofv3 summary profiles/*_busy.txt of the workload
                 while the sources match)
-                achieved TFLOP/s of the attention kernel from HIP events around
-                every timed launch on the stream it runs on, against the peak;
+                achieved TFLOP/s of the attention kernel from one pair of HIP
+                events around the timed launches, on the stream they run on
+                (the average launch duration; events around every launch would
+                add about 7 us of stream work per launch), against the peak;
                 `traffic` is the HBM bytes per launch measured with rocprofv3
                 FETCH_SIZE / WRITE_SIZE (scaled by a copy-kernel calibration),
                 taken from the committed summary in profiles/ for this workload
@@ -100,6 +102,8 @@ def profiled_busy(workload):
 
 
 def time_workload(fa, torch, w, causal, steps, warmup):
+    """Wall time of `steps` forwards on the workload, and their average duration
+    in ms from one pair of HIP events around them on their stream."""
     import workloads
     q, k, v = (x.to("cuda:0") for x in workloads.workload_inputs(w))
     o = torch.empty_like(q)
@@ -108,18 +112,16 @@ def time_workload(fa, torch, w, causal, steps, warmup):
         fa.forward(q, k, v, causal=causal, scale=w.scale, out=o, lse=lse, window=w.window)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(steps):
-        starts[i].record(stream)
+    start.record(stream)
+    for _ in range(steps):
         fa.forward(q, k, v, causal=causal, scale=w.scale, out=o, lse=lse, window=w.window)
-        ends[i].record(stream)
+    end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    kernel_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    return wall, kernel_ms
+    return wall, start.elapsed_time(end) / steps
 
 
 def time_graph(fa, torch, w, causal, launches=20, reps=10):
@@ -195,23 +197,24 @@ def backward_call(fa, torch, w, causal):
 
 
 def time_backward(fa, torch, w, causal, steps, warmup):
-    """HIP-event times of fa_bwd_ex (dQ kernel, then dK/dV kernel) on the workload."""
+    """Wall time of `steps` fa_bwd_ex calls (dQ kernel, then dK/dV kernel) on the
+    workload, and their average duration in ms from one pair of HIP events
+    around them on their stream."""
     call, _ = backward_call(fa, torch, w, causal)
     stream = torch.cuda.current_stream()
     fa.check(call())
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    for i in range(steps):
-        starts[i].record(stream)
+    start.record(stream)
+    for _ in range(steps):
         call()
-        ends[i].record(stream)
+    end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    return wall, [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    return wall, start.elapsed_time(end) / steps
 
 
 def cpu_baseline_backward(w, causal):
@@ -394,11 +397,10 @@ def main():
 
     w = workloads.BY_NAME[args.workload]
     causal = w.causal[-1]
-    wall, kernel_ms = time_workload(fa, torch, w, causal, args.steps, args.warmup)
+    wall, avg_kernel_ms = time_workload(fa, torch, w, causal, args.steps, args.warmup)
     flops = w.flops(causal)
     ms_per_step = wall * 1e3 / args.steps
     value = flops / (wall / args.steps) / 1e12
-    avg_kernel_ms = sum(kernel_ms) / len(kernel_ms)
     achieved = flops / (avg_kernel_ms * 1e-3) / 1e12
     peak = PEAK_MFMA_TFLOPS[w.dtype]
     traffic = args.traffic_bytes if args.traffic_bytes is not None else profiled_traffic(w.name)
@@ -431,7 +433,6 @@ def main():
             "traffic_unit": "bytes per launch (HBM, rocprofv3 FETCH_SIZE + WRITE_SIZE)",
             "algorithmic_bytes": w.hbm_bytes(),
             "kernel_ms_avg": round(avg_kernel_ms, 5),
-            "kernel_ms_min": round(min(kernel_ms), 5),
             "hbm_gbs_algorithmic": round(w.hbm_bytes() / (avg_kernel_ms * 1e-3) / 1e9, 1),
             "mfma_busy_pct": None,
         },
@@ -443,8 +444,7 @@ def main():
     out["roofline"]["valu_active_pct"] = busy.get("valu_active_pct_fwd")
 
     if not args.no_backward and w.dtype in ("f16", "bf16"):
-        bwall, bms = time_backward(fa, torch, w, causal, args.steps, args.warmup)
-        bavg = sum(bms) / len(bms)
+        bwall, bavg = time_backward(fa, torch, w, causal, args.steps, args.warmup)
         bflops = 2.5 * flops  # the usual count: five tile products to the forward's two
         executed = 3.5 * flops  # S and dP are formed by both kernels: seven products
         out["backward"] = {
@@ -465,7 +465,6 @@ def main():
                            else profiled_traffic(w.name + ":backward"),
                 "traffic_unit": "bytes per fa_bwd call (both kernels; HBM, rocprofv3 FETCH_SIZE + WRITE_SIZE)",
                 "kernel_ms_avg": round(bavg, 5),
-                "kernel_ms_min": round(min(bms), 5),
                 "mfma_busy_pct": {"dq": busy.get("mfma_busy_pct_dq"), "dkdv": busy.get("mfma_busy_pct_dkdv")}
                                  if busy else None,
                 "valu_active_pct": {"dq": busy.get("valu_active_pct_dq"), "dkdv": busy.get("valu_active_pct_dkdv")}
