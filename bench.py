@@ -41,8 +41,14 @@ Prints one JSON line.  Also reported:
                 the float64 oracle over every element (--no-configs,
                 --no-parity skip them).
 
+Timing: about 200 ms of untimed launches of the same forward (`settle`,
+--settle-ms; reported in the line) bring a fresh process's GPU to its loaded
+clock, then W untimed warmup steps, then exactly K timed steps between two
+synchronisations (a cold 20-step run reads about 12 % lower: its
+milliseconds run while the clock still rises).
+
 Options: --gpus N (only 1 is supported: the kernel runs on one GPU),
---steps K (timed launches), --warmup W, --workload NAME, --no-cpu-baseline,
+--steps K (timed launches), --warmup W, --settle-ms MS, --workload NAME, --no-cpu-baseline,
 --sweep FILE (also time every named workload and write one JSON line per
 workload to FILE; sweep kernels are timed from a HIP graph of 20 launches
 replayed 10 times, so short kernels carry no host launch overhead).
@@ -101,15 +107,38 @@ def profiled_busy(workload):
     return {}
 
 
-def time_workload(fa, torch, w, causal, steps, warmup):
-    """Wall time of `steps` forwards on the workload, and their average duration
-    in ms from one pair of HIP events around them on their stream."""
+def settle(launch, torch, ms):
+    """Untimed launches for about `ms` of wall time, so that a short timed run
+    starts at the clock the GPU holds under load (a fresh process otherwise
+    times its first milliseconds while the clock still rises).  Returns the
+    milliseconds spent and the launches made."""
+    if ms <= 0:
+        return 0.0, 0
+    t0 = time.perf_counter()
+    n = 0
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(10):
+            launch()
+        n += 10
+        torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3, n
+
+
+def time_workload(fa, torch, w, causal, steps, warmup, settle_ms=0.0):
+    """Wall time of `steps` forwards on the workload, their average duration in
+    ms from one pair of HIP events around them on their stream, and the settle
+    phase (ms, launches) that ran before the `warmup` untimed steps."""
     import workloads
     q, k, v = (x.to("cuda:0") for x in workloads.workload_inputs(w))
     o = torch.empty_like(q)
     lse = torch.empty((w.B, w.H, w.S), dtype=torch.float32, device="cuda:0")
-    for _ in range(warmup):
+
+    def launch():
         fa.forward(q, k, v, causal=causal, scale=w.scale, out=o, lse=lse, window=w.window)
+
+    settled = settle(launch, torch, settle_ms)
+    for _ in range(warmup):
+        launch()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -117,11 +146,11 @@ def time_workload(fa, torch, w, causal, steps, warmup):
     t0 = time.perf_counter()
     start.record(stream)
     for _ in range(steps):
-        fa.forward(q, k, v, causal=causal, scale=w.scale, out=o, lse=lse, window=w.window)
+        launch()
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    return wall, start.elapsed_time(end) / steps
+    return wall, start.elapsed_time(end) / steps, settled
 
 
 def time_graph(fa, torch, w, causal, launches=20, reps=10):
@@ -336,6 +365,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--settle-ms", type=float, default=200.0,
+                    help="untimed launches of the same forward for this long before the warmup steps "
+                         "(0: none), reported as `settle`")
     ap.add_argument("--workload", default="multihead_causal")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward measurement")
@@ -397,7 +429,7 @@ def main():
 
     w = workloads.BY_NAME[args.workload]
     causal = w.causal[-1]
-    wall, avg_kernel_ms = time_workload(fa, torch, w, causal, args.steps, args.warmup)
+    wall, avg_kernel_ms, settled = time_workload(fa, torch, w, causal, args.steps, args.warmup, args.settle_ms)
     flops = w.flops(causal)
     ms_per_step = wall * 1e3 / args.steps
     value = flops / (wall / args.steps) / 1e12
@@ -411,6 +443,9 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle": {"ms": round(settled[0], 1), "launches": settled[1],
+                   "note": "untimed launches of the same forward before the warmup steps, so that the "
+                           "timed steps run at the GPU's loaded clock"},
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
