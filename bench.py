@@ -36,7 +36,8 @@ Prints one JSON line.  Also reported:
   configs       one record per configuration workload and mask (single-head
                 fp32, the headless batch both ways, the multi-head causal
                 workload, the long bf16 sequence, the 20 sweep points): kernel
-                microseconds from a replayed HIP graph, TFLOP/s, fraction of
+                microseconds from a replayed HIP graph (after about 50 ms of
+                untimed replays), TFLOP/s, fraction of
                 peak, algorithmic HBM GB/s, and the errors of O and lse against
                 the float64 oracle over every element (--no-configs,
                 --no-parity skip them).
@@ -153,12 +154,14 @@ def time_workload(fa, torch, w, causal, steps, warmup, settle_ms=0.0):
     return wall, start.elapsed_time(end) / steps, settled
 
 
-def time_graph(fa, torch, w, causal, launches=20, reps=10):
+def time_graph(fa, torch, w, causal, launches=20, reps=10, settle_ms=50.0):
     """Time per forward from a HIP graph of `launches` fa_fwd_ws calls (with the
     workspace fa_fwd_workspace_bytes asks for, as forward() passes it) on
     preallocated buffers, replayed `reps` times between two events: the GPU
     never waits for the host, so short kernels are timed without the Python
-    call's overhead.  Returns the milliseconds per forward."""
+    call's overhead.  Untimed replays for about `settle_ms` first bring the
+    clock back up after the host work between records.  Returns the
+    milliseconds per forward."""
     import workloads
     q, k, v = (x.to("cuda:0") for x in workloads.workload_inputs(w))
     o = torch.empty_like(q)
@@ -184,6 +187,7 @@ def time_graph(fa, torch, w, causal, launches=20, reps=10):
             fa.check(call(side.cuda_stream))
     graph.replay()
     torch.cuda.synchronize()
+    settle(graph.replay, torch, settle_ms)
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
     for _ in range(reps):
@@ -225,13 +229,15 @@ def backward_call(fa, torch, w, causal):
     return call, (dq, dk, dv)
 
 
-def time_backward(fa, torch, w, causal, steps, warmup):
+def time_backward(fa, torch, w, causal, steps, warmup, settle_ms=0.0):
     """Wall time of `steps` fa_bwd_ex calls (dQ kernel, then dK/dV kernel) on the
-    workload, and their average duration in ms from one pair of HIP events
-    around them on their stream."""
+    workload, their average duration in ms from one pair of HIP events around
+    them on their stream, and the settle phase (ms, launches) before the
+    `warmup` untimed calls."""
     call, _ = backward_call(fa, torch, w, causal)
     stream = torch.cuda.current_stream()
     fa.check(call())
+    settled = settle(call, torch, settle_ms)
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
@@ -243,7 +249,7 @@ def time_backward(fa, torch, w, causal, steps, warmup):
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    return wall, start.elapsed_time(end) / steps
+    return wall, start.elapsed_time(end) / steps, settled
 
 
 def cpu_baseline_backward(w, causal):
@@ -479,7 +485,7 @@ def main():
     out["roofline"]["valu_active_pct"] = busy.get("valu_active_pct_fwd")
 
     if not args.no_backward and w.dtype in ("f16", "bf16"):
-        bwall, bavg = time_backward(fa, torch, w, causal, args.steps, args.warmup)
+        bwall, bavg, bsettled = time_backward(fa, torch, w, causal, args.steps, args.warmup, args.settle_ms)
         bflops = 2.5 * flops  # the usual count: five tile products to the forward's two
         executed = 3.5 * flops  # S and dP are formed by both kernels: seven products
         out["backward"] = {
@@ -487,6 +493,7 @@ def main():
             "value": round(bflops / (bwall / args.steps) / 1e12, 2),
             "unit": "TFLOP/s",
             "ms_per_step": round(bwall * 1e3 / args.steps, 5),
+            "settle": {"ms": round(bsettled[0], 1), "launches": bsettled[1]},
             "kernels": ["fa_bwd_dq_kernel", "fa_bwd_dkdv_kernel"],
             "roofline": {
                 "bound": "mfma",

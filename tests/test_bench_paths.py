@@ -38,5 +38,5 @@ def test_backward_call_matches_binding(hkv, window):
     torch.cuda.synchronize()
     assert torch.equal(dq_b, dq) and torch.equal(dk_b, dk) and torch.equal(dv_b, dv)
     # and the timing loop runs on the same call
-    wall, avg_ms = bench.time_backward(fa, torch, w, True, 3, 1)
-    assert wall > 0 and avg_ms > 0
+    wall, avg_ms, (settle_ms, settle_n) = bench.time_backward(fa, torch, w, True, 3, 1, settle_ms=5.0)
+    assert wall > 0 and avg_ms > 0 and settle_ms >= 5.0 and settle_n >= 10
