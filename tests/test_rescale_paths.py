@@ -55,6 +55,9 @@ CASES = [
     (8, 1, 4096, 128, "f16", "one-block kernel, 4-wave workgroups; key split (forward)"),
     (8, 1, 3000, 64, "f16", "thin-grid kernel, 64-row blocks, half-step loop"),
     (8, 1, 1500, 64, "f16", "thin-grid kernel, 32-row blocks, plain loop"),
+    (2, 1, 1024, 16, "f16", "thin-grid kernel, 32-row blocks, one k-step (D = 16)"),
+    (8, 1, 1024, 128, "bf16", "thin-grid kernel, 32-row blocks, accumulators in AGPRs (D = 128)"),
+    (1, 2, 300, 64, "f32", "fp32 matrix-core kernel"),
 ]
 
 
