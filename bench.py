@@ -40,7 +40,10 @@ Prints one JSON line.  Also reported:
                 untimed replays), TFLOP/s, fraction of
                 peak, algorithmic HBM GB/s, and the errors of O and lse against
                 the float64 oracle over every element (--no-configs,
-                --no-parity skip them).
+                --no-parity skip them);
+  extended      the same record for grouped K/V heads (the multi-head causal
+                workload with 4 K/V heads) and a sliding window (B=2 H=16
+                S=8192 D=64 causal, 1024-key left window).
 
 Timing: about 200 ms of untimed launches of the same forward (`settle`,
 --settle-ms; reported in the line) bring a fresh process's GPU to its loaded
@@ -298,9 +301,13 @@ def cpu_baseline(w, causal):
 # the 20-point causal fp16 sweep.
 CONFIG_WORKLOADS = (["single_head_f32", "batch_f16", "multihead_causal", "long_seq_bf16"]
                     + [f"sweep_D{d}_S{s}" for d in (16, 32, 64, 128) for s in (256, 1024, 4096, 8192, 16384)])
+# Grouped K/V heads and a sliding window on full-size problems, recorded beside
+# the configurations (the headline workload with 4 K/V heads; B=2 H=16 S=8192
+# with a 1024-key left window).
+EXTENDED_WORKLOADS = ["gqa_causal", "window_causal"]
 
 
-def config_records(fa, torch, parity=True):
+def config_records(fa, torch, parity=True, names=CONFIG_WORKLOADS):
     """One record per configuration workload and mask: kernel microseconds timed
     from a replayed HIP graph, TFLOP/s, fraction of the dense peak of its dtype,
     algorithmic HBM GB/s and, with parity, the errors of O and lse against the
@@ -309,22 +316,25 @@ def config_records(fa, torch, parity=True):
     import numpy as np
     import workloads
     recs = []
-    for name in CONFIG_WORKLOADS:
+    for name in names:
         w = workloads.BY_NAME[name]
+        win = None if w.window == (-1, -1) else w.window
         for c in w.causal:
             us = time_graph(fa, torch, w, c) * 1e3
             tf = w.flops(c) / (us * 1e-6) / 1e12
             rec = {"workload": name, "causal": c, "dtype": w.dtype, "B": w.B, "H": w.H, "S": w.S, "D": w.D,
+                   **({"H_kv": w.kv_heads} if w.kv_heads != w.H else {}), **({"window": list(win)} if win else {}),
                    "kernel_us": round(us, 2), "tflops": round(tf, 1),
                    "frac": round(tf / PEAK_MFMA_TFLOPS[w.dtype], 4),
                    "hbm_gbs_algorithmic": round(w.hbm_bytes() / (us * 1e-6) / 1e9, 1)}
             if parity:
                 import oracle
                 q, k, v = workloads.workload_inputs(w)
-                o, lse = fa.forward(q.to("cuda:0"), k.to("cuda:0"), v.to("cuda:0"), causal=c, scale=w.scale)
+                o, lse = fa.forward(q.to("cuda:0"), k.to("cuda:0"), v.to("cuda:0"), causal=c, scale=w.scale,
+                                    window=win)
                 torch.cuda.synchronize()
                 o_ref, l_ref = oracle.attention(q.double().numpy(), k.double().numpy(), v.double().numpy(), c,
-                                                w.scale)
+                                                w.scale, win)
                 d_o = np.abs(o.cpu().double().numpy() - o_ref)
                 d_l = np.abs(lse.cpu().double().numpy() - l_ref)
                 rec["max_abs_dO"] = float(d_o.max()) if w.dtype != "f32" else None
@@ -533,6 +543,7 @@ def main():
         out["roofline"]["exp_valu"] = exp_valu_roof(w.D)
     if not args.no_configs:
         out["configs"] = config_records(fa, torch, parity=not args.no_parity)
+        out["extended"] = config_records(fa, torch, parity=not args.no_parity, names=EXTENDED_WORKLOADS)
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, causal)
