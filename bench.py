@@ -43,7 +43,8 @@ Prints one JSON line.  Also reported:
                 --no-parity skip them);
   extended      the same record for grouped K/V heads (the multi-head causal
                 workload with 4 K/V heads) and a sliding window (B=2 H=16
-                S=8192 D=64 causal, 1024-key left window).
+                S=8192 D=64 causal, 1024-key left window), with the backward's
+                event-timed microseconds and fraction of peak on each.
 
 Timing: about 200 ms of untimed launches of the same forward (`settle`,
 --settle-ms; reported in the line) bring a fresh process's GPU to its loaded
@@ -307,7 +308,7 @@ CONFIG_WORKLOADS = (["single_head_f32", "batch_f16", "multihead_causal", "long_s
 EXTENDED_WORKLOADS = ["gqa_causal", "window_causal"]
 
 
-def config_records(fa, torch, parity=True, names=CONFIG_WORKLOADS):
+def config_records(fa, torch, parity=True, names=CONFIG_WORKLOADS, backward=False):
     """One record per configuration workload and mask: kernel microseconds timed
     from a replayed HIP graph, TFLOP/s, fraction of the dense peak of its dtype,
     algorithmic HBM GB/s and, with parity, the errors of O and lse against the
@@ -327,6 +328,12 @@ def config_records(fa, torch, parity=True, names=CONFIG_WORKLOADS):
                    "kernel_us": round(us, 2), "tflops": round(tf, 1),
                    "frac": round(tf / PEAK_MFMA_TFLOPS[w.dtype], 4),
                    "hbm_gbs_algorithmic": round(w.hbm_bytes() / (us * 1e-6) / 1e9, 1)}
+            if backward and w.dtype in ("f16", "bf16"):
+                # the backward on the same problem: 20 calls after 5, event-timed
+                _, bavg, _ = time_backward(fa, torch, w, c, 20, 5, settle_ms=50.0)
+                btf = 2.5 * w.flops(c) / (bavg * 1e-3) / 1e12
+                rec["backward_us"] = round(bavg * 1e3, 2)
+                rec["backward_frac"] = round(btf / PEAK_MFMA_TFLOPS[w.dtype], 4)
             if parity:
                 import oracle
                 q, k, v = workloads.workload_inputs(w)
@@ -543,7 +550,8 @@ def main():
         out["roofline"]["exp_valu"] = exp_valu_roof(w.D)
     if not args.no_configs:
         out["configs"] = config_records(fa, torch, parity=not args.no_parity)
-        out["extended"] = config_records(fa, torch, parity=not args.no_parity, names=EXTENDED_WORKLOADS)
+        out["extended"] = config_records(fa, torch, parity=not args.no_parity, names=EXTENDED_WORKLOADS,
+                                         backward=not args.no_backward)
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, causal)
